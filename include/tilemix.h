@@ -1,0 +1,158 @@
+/*
+ * tilemix.h - C ABI of libtilemix.so: tile-group precision-routed fused prefill attention
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one defined in "TileMix: Tile-Centric Mixed-Precision Attention for LLM
+ * Inference Acceleration" (arXiv 2608.17336): the L_q x L_k score matrix is cut into route tiles
+ * of BM_r x BN_r; a packed bitmask selects, per (KV head, query-tile row, key-tile group), either
+ * an FP16 QK^T or an INT8 QK^T with int32 accumulation and per-token scale restoration; both
+ * paths feed one online-softmax state (row max, normaliser, output accumulator) before an FP16
+ * P.V (Sections 3.1, 4.1-4.3).
+ *
+ * Conventions shared by every call:
+ *   - All tensor pointers are DEVICE pointers owned by the caller. The library allocates no
+ *     device memory and keeps no state other than a thread-local error string.
+ *   - Calls are asynchronous: they validate the host-side arguments, enqueue kernels on `stream`
+ *     (a hipStream_t; NULL = the null stream) and return. The caller synchronises.
+ *     The contents of device arrays (cu_seqlens values, route bits) are not validated; values
+ *     that contradict the host-side sizes are undefined behaviour.
+ *   - Results are bitwise deterministic run to run (no atomics).
+ *   - Token-major layouts: a fp16 or int8 tensor of `n` tokens and `h` heads of `d` channels is
+ *     [n, h, d]; fp16 inputs may carry element strides for the token and head dimensions
+ *     (channel stride 1). Per-token scales are head-major [h, n] fp32.
+ *   - Every call returns TILEMIX_OK or an error status; tilemix_last_error() then describes it.
+ */
+#ifndef TILEMIX_H
+#define TILEMIX_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TILEMIX_OK = 0,
+  TILEMIX_EINVAL = 1,       /* an argument is out of range, inconsistent or NULL when required */
+  TILEMIX_EUNSUPPORTED = 2, /* a valid request outside what the kernels implement (e.g. head_dim) */
+  TILEMIX_ELAUNCH = 3       /* a HIP launch error was reported */
+} tilemix_status;
+
+/* Text of the last non-OK status returned on the calling thread ("" if none). The pointer stays
+ * valid until the next tilemix call on the same thread. */
+const char* tilemix_last_error(void);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int32_t tilemix_version(void);
+
+/*
+ * tilemix_quantize_qk - the quantize-once pass (Section 4.3 "quantize-once mode"; the
+ * quantizer psi of Section 3.2 taken per token and per head).
+ *
+ * For every token t and head h, with x = the head_dim fp16 channels of that row:
+ *   a = max_c |x_c|;  a == 0 -> scale = 0, codes = 0;
+ *   otherwise inv = 127/a and scale = a/127 (correctly rounded fp32 divisions),
+ *   code_c = clamp(rint(x_c * inv), -127, 127)   (fp32 product, round half to even).
+ *
+ *   q       fp16 [total_q, hq, head_dim] with element strides q_stride_tok / q_stride_head
+ *   q8      int8 [total_q, hq, head_dim] contiguous (output)
+ *   q_scale fp32 [hq, total_q]            (output)
+ * and the same for k / k8 / k_scale with total_k, hk. Either group may be skipped by passing
+ * NULL input AND output pointers for it (e.g. only K and V of an INT8 cache, or only Q).
+ * head_dim must be 64 or 128 (TILEMIX_EUNSUPPORTED otherwise).
+ */
+tilemix_status tilemix_quantize_qk(const void* q, int64_t total_q, int32_t hq,
+                                   int64_t q_stride_tok, int64_t q_stride_head, int8_t* q8,
+                                   float* q_scale, const void* k, int64_t total_k, int32_t hk,
+                                   int64_t k_stride_tok, int64_t k_stride_head, int8_t* k8,
+                                   float* k_scale, int32_t head_dim, void* stream);
+
+/*
+ * tilemix_pack_route_mask - packs a routing map into bitmask words (Section 4.2, packing and
+ * lookup equations: b = sum_j R_j 2^j, R_j = (b >> j) & 1).
+ *
+ *   route  uint8 [rows, t_mask], each 1 (INT8 path) or 0 (FP16 path); rows = hk * total_mtiles
+ *          in the order [h_k][route row].
+ *   words  uint64 [rows, words_per_row] (output). Group g lives in word g >> 6 at bit g & 63;
+ *          bits at or above t_mask are written 0. words_per_row >= ceil(t_mask / 64).
+ * Bytes other than 0/1 in `route` are treated as 1 (any nonzero = INT8).
+ */
+tilemix_status tilemix_pack_route_mask(const uint8_t* route, int64_t rows, int32_t t_mask,
+                                       uint64_t* words, int32_t words_per_row, void* stream);
+
+typedef struct tilemix_fwd_params {
+  uint32_t struct_size;         /* sizeof(tilemix_fwd_params) */
+  int32_t batch;                /* number of sequences, >= 1 */
+  int32_t hq, hkv;              /* query / KV heads; hq % hkv == 0; h_k = h_q / (hq / hkv) */
+  int32_t head_dim;             /* 64 or 128 */
+  int64_t total_q, total_k;     /* tokens over all sequences */
+  int32_t max_seqlen_q;         /* >= every L_q,b (sizes the grid) */
+  int32_t max_seqlen_k;         /* >= every L_k,b */
+  const int32_t* cu_seqlens_q;  /* device [batch+1], prefix sums of L_q,b */
+  const int32_t* cu_seqlens_k;  /* device [batch+1], prefix sums of L_k,b */
+  const int32_t* cu_mtiles;     /* device [batch+1], prefix sums of ceil(L_q,b / route_block_m) */
+  int32_t total_mtiles;         /* cu_mtiles[batch] */
+
+  const void* q;                /* fp16 [total_q, hq, d] (strided) - FP16 score path */
+  int64_t q_stride_tok, q_stride_head;
+  const void* k;                /* fp16 [total_k, hkv, d] (strided); NULL iff kv_int8 */
+  int64_t k_stride_tok, k_stride_head;
+  const void* v;                /* fp16 [total_k, hkv, d] (strided); NULL iff kv_int8 */
+  int64_t v_stride_tok, v_stride_head;
+
+  const int8_t* q8;             /* [total_q, hq, d], from tilemix_quantize_qk */
+  const float* q_scale;         /* [hq, total_q] */
+  const int8_t* k8;             /* [total_k, hkv, d] */
+  const float* k_scale;         /* [hkv, total_k] */
+  const int8_t* v8;             /* [total_k, hkv, d]; kv_int8 only (V = v_scale * v8) */
+  const float* v_scale;         /* [hkv, total_k];    kv_int8 only */
+  int32_t kv_int8;              /* 1: K/V are an INT8 cache (K = k_scale*k8, V = v_scale*v8) */
+
+  const uint64_t* route_words;  /* [hkv, total_mtiles, words_per_row], from pack */
+  int32_t words_per_row;        /* >= ceil(T_mask / 64) for every sequence */
+  int32_t route_block_m;        /* BM_r: query rows per route tile, multiple of 32 */
+  int32_t route_block_n;        /* BN_r: keys per key tile, multiple of 64 */
+  int32_t route_group;          /* g >= 1: key tiles per routing bit; g_j = floor(n / g) */
+
+  int32_t causal;               /* 1: key j legal for query i iff j <= i + (L_k - L_q) */
+  float softmax_scale;          /* <= 0 selects 1/sqrt(head_dim) */
+
+  void* out;                    /* [total_q, hq, d] contiguous, fp16 or fp32 (output) */
+  int32_t out_dtype;            /* 0 = fp16, 1 = fp32 */
+  float* lse;                   /* optional [hq, total_q] natural-log sum-exp (output) */
+
+  /* Optional debug dump of the raw int32 accumulators of INT8-routed tiles for one query head:
+   * dump[r - debug_mtile_begin][n][ii][jj], shape [debug_mtile_count, debug_ntiles_max,
+   * route_block_m, route_block_n], for route rows r in [begin, begin+count) and key tiles n.
+   * Every element the kernel computes for an INT8-routed tile is written (masked positions of
+   * diagonal tiles included); FP16-routed tiles, skipped tiles and out-of-sequence elements are
+   * left untouched, so the caller pre-fills a sentinel. NULL disables it. */
+  int32_t* debug_s32;
+  int32_t debug_head, debug_mtile_begin, debug_mtile_count, debug_ntiles_max;
+} tilemix_fwd_params;
+
+/*
+ * tilemix_prefill_fwd - the fused routed attention (Sections 4.1 and 4.3).
+ *
+ * For each sequence b, query head h_q and query i < L_q,b, with h_k = h_q / (hq/hkv) and
+ * key tile n = floor(j / BN_r), group g_j = floor(n / g), route row r = cu_mtiles[b] +
+ * floor(i / BM_r) and bit R = (route_words[h_k][r][g_j >> 6] >> (g_j & 63)) & 1:
+ *   s_ij = q_scale[h_q][i] * k_scale[h_k][j] * (q8_i . k8_j) * softmax_scale    if R = 1
+ *   s_ij = (q_i . K_j) * softmax_scale                                         if R = 0
+ * (K_j = fp16 K, or k_scale*k8 with kv_int8), over the legal keys j; then
+ * O_i = sum_j softmax(s_i)_j V_j and LSE_i = log sum_j exp(s_ij). A query with no legal key
+ * gets O = 0 and LSE = -inf. Scores, softmax state and the P.V accumulator are fp32; P is
+ * rounded to fp16 for the FP16 P.V product.
+ *
+ * Errors: EINVAL for a NULL required pointer, struct_size mismatch, hq % hkv != 0,
+ * route_block_m not a multiple of 32, route_block_n not a multiple of 64, route_group < 1,
+ * words_per_row < 1, kv_int8 with non-NULL k/v (or without v8/v_scale), a bad debug range;
+ * EUNSUPPORTED for head_dim other than 64/128.
+ */
+tilemix_status tilemix_prefill_fwd(const tilemix_fwd_params* params, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TILEMIX_H */

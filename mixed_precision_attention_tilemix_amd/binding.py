@@ -1,0 +1,195 @@
+"""Thin ctypes binding of libtilemix.so (include/tilemix.h).
+
+The functions here carry the C names and only marshal arguments: they take torch tensors that
+already live on the GPU, pass their device pointers, sizes and the current HIP stream to the
+library, and raise ``TilemixError`` on a non-OK status. Every step of the computation runs in
+the library's HIP kernels; there is no fallback of any kind. If the library has not been built,
+importing this module succeeds but the first call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtilemix.so")
+_lib = None
+
+TILEMIX_OK, TILEMIX_EINVAL, TILEMIX_EUNSUPPORTED, TILEMIX_ELAUNCH = 0, 1, 2, 3
+
+# The entry points declared in include/tilemix.h.
+EXPORTED = ("tilemix_last_error", "tilemix_version", "tilemix_quantize_qk",
+            "tilemix_pack_route_mask", "tilemix_prefill_fwd")
+
+
+class TilemixError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"tilemix status {status}: {message}")
+        self.status = status
+
+
+class FwdParams(ctypes.Structure):
+    """Mirror of tilemix_fwd_params."""
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("batch", ctypes.c_int32),
+        ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("total_q", ctypes.c_int64), ("total_k", ctypes.c_int64),
+        ("max_seqlen_q", ctypes.c_int32), ("max_seqlen_k", ctypes.c_int32),
+        ("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_k", ctypes.c_void_p),
+        ("cu_mtiles", ctypes.c_void_p),
+        ("total_mtiles", ctypes.c_int32),
+        ("q", ctypes.c_void_p), ("q_stride_tok", ctypes.c_int64), ("q_stride_head", ctypes.c_int64),
+        ("k", ctypes.c_void_p), ("k_stride_tok", ctypes.c_int64), ("k_stride_head", ctypes.c_int64),
+        ("v", ctypes.c_void_p), ("v_stride_tok", ctypes.c_int64), ("v_stride_head", ctypes.c_int64),
+        ("q8", ctypes.c_void_p), ("q_scale", ctypes.c_void_p),
+        ("k8", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
+        ("v8", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+        ("kv_int8", ctypes.c_int32),
+        ("route_words", ctypes.c_void_p),
+        ("words_per_row", ctypes.c_int32),
+        ("route_block_m", ctypes.c_int32), ("route_block_n", ctypes.c_int32),
+        ("route_group", ctypes.c_int32),
+        ("causal", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("out", ctypes.c_void_p), ("out_dtype", ctypes.c_int32),
+        ("lse", ctypes.c_void_p),
+        ("debug_s32", ctypes.c_void_p),
+        ("debug_head", ctypes.c_int32), ("debug_mtile_begin", ctypes.c_int32),
+        ("debug_mtile_count", ctypes.c_int32), ("debug_ntiles_max", ctypes.c_int32),
+    ]
+
+
+def load(path: Optional[str] = None):
+    """Load libtilemix.so (once). Raises FileNotFoundError if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise FileNotFoundError(f"{path} is missing: build it with __graft_entry__.build() "
+                                "(hipcc, gfx950); there is no fallback path")
+    L = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    L.tilemix_last_error.restype = ctypes.c_char_p
+    L.tilemix_last_error.argtypes = []
+    L.tilemix_version.restype = i32
+    L.tilemix_version.argtypes = []
+    L.tilemix_quantize_qk.restype = ctypes.c_int
+    L.tilemix_quantize_qk.argtypes = [vp, i64, i32, i64, i64, vp, vp,
+                                      vp, i64, i32, i64, i64, vp, vp, i32, vp]
+    L.tilemix_pack_route_mask.restype = ctypes.c_int
+    L.tilemix_pack_route_mask.argtypes = [vp, i64, i32, vp, i32, vp]
+    L.tilemix_prefill_fwd.restype = ctypes.c_int
+    L.tilemix_prefill_fwd.argtypes = [ctypes.POINTER(FwdParams), vp]
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != TILEMIX_OK:
+        raise TilemixError(status, load().tilemix_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tilemix takes device tensors only")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _tok_head_strides(x: torch.Tensor):
+    if x.dim() != 3 or x.stride(2) != 1:
+        raise ValueError("expected [tokens, heads, head_dim] with unit channel stride")
+    return x.stride(0), x.stride(1)
+
+
+def last_error() -> str:
+    return load().tilemix_last_error().decode()
+
+
+def version() -> int:
+    return int(load().tilemix_version())
+
+
+def tilemix_quantize_qk(q: Optional[torch.Tensor] = None, q8: Optional[torch.Tensor] = None,
+                        q_scale: Optional[torch.Tensor] = None, k: Optional[torch.Tensor] = None,
+                        k8: Optional[torch.Tensor] = None, k_scale: Optional[torch.Tensor] = None,
+                        stream=None) -> None:
+    """q fp16 [T, Hq, d] -> q8 int8 [T, Hq, d], q_scale fp32 [Hq, T]; same for k (either optional)."""
+    ref = q if q is not None else k
+    d = ref.shape[2]
+    qs = _tok_head_strides(q) if q is not None else (0, 0)
+    ks = _tok_head_strides(k) if k is not None else (0, 0)
+    _check(load().tilemix_quantize_qk(
+        _ptr(q), q.shape[0] if q is not None else 0, q.shape[1] if q is not None else 0,
+        qs[0], qs[1], _ptr(q8), _ptr(q_scale),
+        _ptr(k), k.shape[0] if k is not None else 0, k.shape[1] if k is not None else 0,
+        ks[0], ks[1], _ptr(k8), _ptr(k_scale), d, _stream(stream)))
+
+
+def tilemix_pack_route_mask(route: torch.Tensor, words: torch.Tensor, stream=None) -> None:
+    """route uint8 [..., t_mask] -> words (int64 storage of uint64) [..., words_per_row]."""
+    t_mask = route.shape[-1]
+    rows = route.numel() // t_mask if t_mask else words.numel() // words.shape[-1]
+    _check(load().tilemix_pack_route_mask(_ptr(route), rows, t_mask, _ptr(words),
+                                          words.shape[-1], _stream(stream)))
+
+
+def tilemix_prefill_fwd(*, q, q8, q_scale, k8, k_scale, route_words, cu_seqlens_q, cu_seqlens_k,
+                        cu_mtiles, max_seqlen_q: int, max_seqlen_k: int, route_block_m: int,
+                        route_block_n: int, route_group: int, out, k=None, v=None, v8=None,
+                        v_scale=None, causal: bool = True, softmax_scale: float = 0.0, lse=None,
+                        debug_s32=None, debug_head: int = 0, debug_mtile_begin: int = 0,
+                        debug_mtile_count: int = 0, stream=None) -> None:
+    """Fill tilemix_fwd_params from device tensors and call tilemix_prefill_fwd."""
+    kv_int8 = v8 is not None
+    qs = _tok_head_strides(q)
+    ks = _tok_head_strides(k) if k is not None else (0, 0)
+    vs = _tok_head_strides(v) if v is not None else (0, 0)
+    p = FwdParams()
+    p.struct_size = ctypes.sizeof(FwdParams)
+    p.batch = cu_seqlens_q.shape[0] - 1
+    p.hq = q.shape[1]
+    p.hkv = k8.shape[1]
+    p.head_dim = q.shape[2]
+    p.total_q = q.shape[0]
+    p.total_k = k8.shape[0]
+    p.max_seqlen_q = int(max_seqlen_q)
+    p.max_seqlen_k = int(max_seqlen_k)
+    p.cu_seqlens_q = _ptr(cu_seqlens_q)
+    p.cu_seqlens_k = _ptr(cu_seqlens_k)
+    p.cu_mtiles = _ptr(cu_mtiles)
+    p.total_mtiles = route_words.shape[1]
+    p.q, (p.q_stride_tok, p.q_stride_head) = _ptr(q), qs
+    p.k, (p.k_stride_tok, p.k_stride_head) = _ptr(k), ks
+    p.v, (p.v_stride_tok, p.v_stride_head) = _ptr(v), vs
+    p.q8, p.q_scale = _ptr(q8), _ptr(q_scale)
+    p.k8, p.k_scale = _ptr(k8), _ptr(k_scale)
+    p.v8, p.v_scale = _ptr(v8), _ptr(v_scale)
+    p.kv_int8 = int(kv_int8)
+    p.route_words = _ptr(route_words)
+    p.words_per_row = route_words.shape[2]
+    p.route_block_m, p.route_block_n, p.route_group = route_block_m, route_block_n, route_group
+    p.causal = int(bool(causal))
+    p.softmax_scale = float(softmax_scale)
+    p.out = _ptr(out)
+    p.out_dtype = 1 if out.dtype == torch.float32 else 0
+    p.lse = _ptr(lse)
+    p.debug_s32 = _ptr(debug_s32)
+    if debug_s32 is not None:
+        p.debug_head, p.debug_mtile_begin = debug_head, debug_mtile_begin
+        p.debug_mtile_count, p.debug_ntiles_max = debug_mtile_count, debug_s32.shape[1]
+    _check(load().tilemix_prefill_fwd(ctypes.byref(p), _stream(stream)))

@@ -1,0 +1,209 @@
+// C ABI of libtilemix (declared in include/tilemix.h): host-side argument validation, the
+// thread-local error string and the kernel launches. No device memory is allocated here.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/tilemix.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+tilemix_status fail(tilemix_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+tilemix_status ok() {
+  g_last_error.clear();
+  return TILEMIX_OK;
+}
+
+tilemix_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(TILEMIX_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+tilemix_status check_quant_group(const char* name, const void* x, int64_t n, int32_t h,
+                                 int64_t st_tok, int64_t st_head, const int8_t* x8,
+                                 const float* s, int32_t d) {
+  if (x == nullptr && x8 == nullptr && s == nullptr) return TILEMIX_OK;
+  if (x == nullptr || x8 == nullptr || s == nullptr)
+    return fail(TILEMIX_EINVAL, "quantize_qk: %s input and both outputs must be all set or all NULL", name);
+  if (n < 0 || h < 1) return fail(TILEMIX_EINVAL, "quantize_qk: %s has n_tok=%lld heads=%d", name, (long long)n, h);
+  if (st_tok < 0 || st_head < 0 || st_tok % 8 || st_head % 8)
+    return fail(TILEMIX_EINVAL, "quantize_qk: %s strides must be non-negative multiples of 8 elements", name);
+  if (!aligned(x, 16) || !aligned(x8, 8) || !aligned(s, 4))
+    return fail(TILEMIX_EINVAL, "quantize_qk: %s pointers misaligned (need 16/8/4 bytes)", name);
+  (void)d;
+  return TILEMIX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tilemix_last_error(void) { return g_last_error.c_str(); }
+
+int32_t tilemix_version(void) { return 100; }
+
+tilemix_status tilemix_quantize_qk(const void* q, int64_t total_q, int32_t hq,
+                                   int64_t q_stride_tok, int64_t q_stride_head, int8_t* q8,
+                                   float* q_scale, const void* k, int64_t total_k, int32_t hk,
+                                   int64_t k_stride_tok, int64_t k_stride_head, int8_t* k8,
+                                   float* k_scale, int32_t head_dim, void* stream) {
+  if (head_dim != 64 && head_dim != 128)
+    return fail(TILEMIX_EUNSUPPORTED, "quantize_qk: head_dim %d (supported: 64, 128)", head_dim);
+  tilemix_status st;
+  if ((st = check_quant_group("q", q, total_q, hq, q_stride_tok, q_stride_head, q8, q_scale, head_dim)))
+    return st;
+  if ((st = check_quant_group("k", k, total_k, hk, k_stride_tok, k_stride_head, k8, k_scale, head_dim)))
+    return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (q) {
+    hipError_t e = tilemix::launch_quantize(q, total_q, hq, q_stride_tok, q_stride_head, q8,
+                                            q_scale, head_dim, s);
+    if (e != hipSuccess) return from_hip(e, "quantize_qk(q)");
+  }
+  if (k) {
+    hipError_t e = tilemix::launch_quantize(k, total_k, hk, k_stride_tok, k_stride_head, k8,
+                                            k_scale, head_dim, s);
+    if (e != hipSuccess) return from_hip(e, "quantize_qk(k)");
+  }
+  return ok();
+}
+
+tilemix_status tilemix_pack_route_mask(const uint8_t* route, int64_t rows, int32_t t_mask,
+                                       uint64_t* words, int32_t words_per_row, void* stream) {
+  if (rows < 0 || t_mask < 0) return fail(TILEMIX_EINVAL, "pack_route_mask: negative size");
+  if (words_per_row < 1 || static_cast<int64_t>(t_mask) > 64LL * words_per_row)
+    return fail(TILEMIX_EINVAL, "pack_route_mask: t_mask %d does not fit %d words per row", t_mask,
+                words_per_row);
+  if (rows > 0 && (words == nullptr || (t_mask > 0 && route == nullptr)))
+    return fail(TILEMIX_EINVAL, "pack_route_mask: NULL route or words");
+  if (!aligned(words, 8)) return fail(TILEMIX_EINVAL, "pack_route_mask: words misaligned");
+  return from_hip(tilemix::launch_pack(route, rows, t_mask, words, words_per_row,
+                                       static_cast<hipStream_t>(stream)),
+                  "pack_route_mask");
+}
+
+tilemix_status tilemix_prefill_fwd(const tilemix_fwd_params* p, void* stream) {
+  if (p == nullptr) return fail(TILEMIX_EINVAL, "prefill_fwd: NULL params");
+  if (p->struct_size != sizeof(tilemix_fwd_params))
+    return fail(TILEMIX_EINVAL, "prefill_fwd: struct_size %u != %zu", p->struct_size,
+                sizeof(tilemix_fwd_params));
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(TILEMIX_EUNSUPPORTED, "prefill_fwd: head_dim %d (supported: 64, 128)", p->head_dim);
+  if (p->batch < 1 || p->hq < 1 || p->hkv < 1 || p->hq % p->hkv)
+    return fail(TILEMIX_EINVAL, "prefill_fwd: batch=%d hq=%d hkv=%d (need hq %% hkv == 0)", p->batch,
+                p->hq, p->hkv);
+  if (p->total_q < 0 || p->total_k < 0 || p->max_seqlen_q < 0 || p->max_seqlen_k < 0 ||
+      p->total_mtiles < 0)
+    return fail(TILEMIX_EINVAL, "prefill_fwd: negative size");
+  if (p->route_block_m < 32 || p->route_block_m % 32)
+    return fail(TILEMIX_EINVAL, "prefill_fwd: route_block_m %d is not a positive multiple of 32",
+                p->route_block_m);
+  if (p->route_block_n < 64 || p->route_block_n % 64)
+    return fail(TILEMIX_EINVAL, "prefill_fwd: route_block_n %d is not a positive multiple of 64",
+                p->route_block_n);
+  if (p->route_group < 1) return fail(TILEMIX_EINVAL, "prefill_fwd: route_group %d < 1", p->route_group);
+  if (p->words_per_row < 1) return fail(TILEMIX_EINVAL, "prefill_fwd: words_per_row < 1");
+  const int64_t t_mask = ceil_div(p->max_seqlen_k, static_cast<int64_t>(p->route_block_n) * p->route_group);
+  if (t_mask > 64LL * p->words_per_row)
+    return fail(TILEMIX_EINVAL, "prefill_fwd: %lld key-tile groups need more than %d words per row",
+                (long long)t_mask, p->words_per_row);
+  if (!p->cu_seqlens_q || !p->cu_seqlens_k || !p->cu_mtiles || !p->q || !p->q8 || !p->q_scale ||
+      !p->k8 || !p->k_scale || !p->route_words || !p->out)
+    return fail(TILEMIX_EINVAL, "prefill_fwd: a required pointer is NULL");
+  if (p->kv_int8) {
+    if (p->k || p->v)
+      return fail(TILEMIX_EINVAL, "prefill_fwd: kv_int8 takes K/V from k8/v8; k and v must be NULL");
+    if (!p->v8 || !p->v_scale) return fail(TILEMIX_EINVAL, "prefill_fwd: kv_int8 needs v8 and v_scale");
+  } else {
+    if (!p->k || !p->v) return fail(TILEMIX_EINVAL, "prefill_fwd: fp16 k and v are required");
+  }
+  if (p->out_dtype != 0 && p->out_dtype != 1)
+    return fail(TILEMIX_EINVAL, "prefill_fwd: out_dtype %d (0 = fp16, 1 = fp32)", p->out_dtype);
+  // 16-byte vector access of the fp16 / int8 rows
+  const int64_t st[6] = {p->q_stride_tok, p->q_stride_head, p->k_stride_tok, p->k_stride_head,
+                         p->v_stride_tok, p->v_stride_head};
+  for (int i = 0; i < 6; ++i) {
+    if (i >= 2 && p->kv_int8) break;
+    if (st[i] < 0 || st[i] % 8) return fail(TILEMIX_EINVAL, "prefill_fwd: fp16 strides must be multiples of 8");
+  }
+  if (!aligned(p->q, 16) || (p->k && !aligned(p->k, 16)) || (p->v && !aligned(p->v, 16)) ||
+      !aligned(p->q8, 16) || !aligned(p->k8, 16) || (p->v8 && !aligned(p->v8, 16)) ||
+      !aligned(p->out, 16) || !aligned(p->k_scale, 4) || (p->v_scale && !aligned(p->v_scale, 4)))
+    return fail(TILEMIX_EINVAL, "prefill_fwd: tensors must be 16-byte aligned");
+  if (p->debug_s32) {
+    if (p->debug_head < 0 || p->debug_head >= p->hq || p->debug_mtile_begin < 0 ||
+        p->debug_mtile_count < 0 || p->debug_mtile_begin + p->debug_mtile_count > p->total_mtiles)
+      return fail(TILEMIX_EINVAL, "prefill_fwd: debug head/route-row range out of bounds");
+    if (p->debug_ntiles_max < ceil_div(p->max_seqlen_k, p->route_block_n))
+      return fail(TILEMIX_EINVAL, "prefill_fwd: debug_ntiles_max %d < ceil(max_seqlen_k / route_block_n)",
+                  p->debug_ntiles_max);
+  }
+  if (p->total_q == 0 || p->max_seqlen_q == 0) return ok();
+
+  const float scale = p->softmax_scale > 0.0f ? p->softmax_scale
+                                              : 1.0f / std::sqrt(static_cast<float>(p->head_dim));
+  tilemix::FwdArgs a{};
+  a.hq = p->hq;
+  a.hkv = p->hkv;
+  a.total_q = p->total_q;
+  a.total_k = p->total_k;
+  a.max_seqlen_q = p->max_seqlen_q;
+  a.cu_q = p->cu_seqlens_q;
+  a.cu_k = p->cu_seqlens_k;
+  a.cu_mtiles = p->cu_mtiles;
+  a.total_mtiles = p->total_mtiles;
+  a.q = static_cast<const _Float16*>(p->q);
+  a.q_stride_tok = p->q_stride_tok;
+  a.q_stride_head = p->q_stride_head;
+  a.k = static_cast<const _Float16*>(p->k);
+  a.k_stride_tok = p->k_stride_tok;
+  a.k_stride_head = p->k_stride_head;
+  a.v = static_cast<const _Float16*>(p->v);
+  a.v_stride_tok = p->v_stride_tok;
+  a.v_stride_head = p->v_stride_head;
+  a.q8 = p->q8;
+  a.q_scale = p->q_scale;
+  a.k8 = p->k8;
+  a.k_scale = p->k_scale;
+  a.v8 = p->v8;
+  a.v_scale = p->v_scale;
+  a.words = p->route_words;
+  a.wpr = p->words_per_row;
+  a.bm_r = p->route_block_m;
+  a.bn_r = p->route_block_n;
+  a.group = p->route_group;
+  a.causal = p->causal ? 1 : 0;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out = p->out;
+  a.out_f32 = p->out_dtype == 1;
+  a.lse = p->lse;
+  a.dump = p->debug_s32;
+  a.dump_head = p->debug_head;
+  a.dump_m0 = p->debug_mtile_begin;
+  a.dump_mcount = p->debug_mtile_count;
+  a.dump_ntiles = p->debug_ntiles_max;
+  return from_hip(tilemix::launch_prefill(a, p->batch, p->head_dim, p->kv_int8 != 0,
+                                          static_cast<hipStream_t>(stream)),
+                  "prefill_fwd");
+}
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// Host-side launchers of the libtilemix kernels (internal; the public ABI is include/tilemix.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tilemix {
+
+// Per-token symmetric INT8 quantization of n_tok x n_head rows of head_dim fp16 values.
+hipError_t launch_quantize(const void* x, int64_t n_tok, int32_t n_head, int64_t stride_tok,
+                           int64_t stride_head, int8_t* x8, float* scale, int32_t head_dim,
+                           hipStream_t stream);
+
+hipError_t launch_pack(const uint8_t* route, int64_t rows, int32_t t_mask, uint64_t* words,
+                       int32_t words_per_row, hipStream_t stream);
+
+// Everything the fused kernel reads, by value.
+struct FwdArgs {
+  int32_t hq, hkv;
+  int64_t total_q, total_k;
+  int32_t max_seqlen_q;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const int32_t* cu_mtiles;
+  int32_t total_mtiles;
+  const _Float16* q;
+  int64_t q_stride_tok, q_stride_head;
+  const _Float16* k;
+  int64_t k_stride_tok, k_stride_head;
+  const _Float16* v;
+  int64_t v_stride_tok, v_stride_head;
+  const int8_t* q8;
+  const float* q_scale;
+  const int8_t* k8;
+  const float* k_scale;
+  const int8_t* v8;
+  const float* v_scale;
+  const uint64_t* words;
+  int32_t wpr, bm_r, bn_r, group;
+  int32_t causal;
+  float scale_log2;  // softmax_scale * log2(e)
+  void* out;
+  int32_t out_f32;
+  float* lse;
+  int32_t* dump;
+  int32_t dump_head, dump_m0, dump_mcount, dump_ntiles;
+};
+
+hipError_t launch_prefill(const FwdArgs& a, int32_t batch, int32_t head_dim, bool kv_int8,
+                          hipStream_t stream);
+
+}  // namespace tilemix

@@ -1,0 +1,81 @@
+"""Device-side plumbing around the three library calls: upload a workload, allocate the
+outputs with torch, and run one pass of the hot path (quantize-once, pack, fused attention)."""
+
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+
+class DeviceProblem:
+    """A workload resident in device memory plus its outputs.
+
+    ``step()`` is one pass of the hot path: tilemix_quantize_qk (Q, and K unless K/V arrive as
+    an INT8 cache), tilemix_pack_route_mask and tilemix_prefill_fwd, all enqueued on the current
+    stream. With ``kv_int8`` the INT8 K/V cache is produced once at construction by the library's
+    own quantizer, and the fp16 K/V are dropped."""
+
+    def __init__(self, w, device: str = "cuda", out_dtype=torch.float32, with_lse: bool = True,
+                 softmax_scale: float = 0.0):
+        self.w = w
+        dev = torch.device(device)
+        T, hq, hk, d = w.total, w.hq, w.hk, w.d
+        self.q = torch.from_numpy(w.q).to(dev)
+        self.cu = torch.from_numpy(w.cu_seqlens).to(dev)
+        self.cu_mtiles = torch.from_numpy(w.cu_mtiles).to(dev)
+        self.route = torch.from_numpy(np.ascontiguousarray(w.route)).to(dev)
+        self.q8 = torch.empty((T, hq, d), dtype=torch.int8, device=dev)
+        self.q_scale = torch.empty((hq, T), dtype=torch.float32, device=dev)
+        self.k8 = torch.empty((T, hk, d), dtype=torch.int8, device=dev)
+        self.k_scale = torch.empty((hk, T), dtype=torch.float32, device=dev)
+        self.words = torch.empty((hk, w.total_mtiles, w.words_per_row), dtype=torch.int64, device=dev)
+        self.out = torch.empty((T, hq, d), dtype=out_dtype, device=dev)
+        self.lse = torch.empty((hq, T), dtype=torch.float32, device=dev) if with_lse else None
+        self.softmax_scale = softmax_scale
+        self.max_seqlen = max(w.seqlens) if w.seqlens else 0
+        if w.kv_int8:
+            k = torch.from_numpy(w.k).to(dev)
+            v = torch.from_numpy(w.v).to(dev)
+            self.v8 = torch.empty((T, hk, d), dtype=torch.int8, device=dev)
+            self.v_scale = torch.empty((hk, T), dtype=torch.float32, device=dev)
+            B.tilemix_quantize_qk(q=v, q8=self.v8, q_scale=self.v_scale, k=k, k8=self.k8,
+                                  k_scale=self.k_scale)
+            del k, v
+            self.k = self.v = None
+        else:
+            self.k = torch.from_numpy(w.k).to(dev)
+            self.v = torch.from_numpy(w.v).to(dev)
+            self.v8 = self.v_scale = None
+
+    def quantize(self, stream=None):
+        if self.w.kv_int8:
+            B.tilemix_quantize_qk(q=self.q, q8=self.q8, q_scale=self.q_scale, stream=stream)
+        else:
+            B.tilemix_quantize_qk(q=self.q, q8=self.q8, q_scale=self.q_scale, k=self.k, k8=self.k8,
+                                  k_scale=self.k_scale, stream=stream)
+
+    def pack(self, stream=None):
+        B.tilemix_pack_route_mask(self.route.view(-1, self.route.shape[-1]),
+                                  self.words.view(-1, self.words.shape[-1]), stream=stream)
+
+    def attention(self, stream=None, debug_s32: Optional[torch.Tensor] = None, debug_head: int = 0,
+                  debug_mtile_begin: int = 0, debug_mtile_count: int = 0):
+        w = self.w
+        B.tilemix_prefill_fwd(
+            q=self.q, k=self.k, v=self.v, q8=self.q8, q_scale=self.q_scale, k8=self.k8,
+            k_scale=self.k_scale, v8=self.v8, v_scale=self.v_scale, route_words=self.words,
+            cu_seqlens_q=self.cu, cu_seqlens_k=self.cu, cu_mtiles=self.cu_mtiles,
+            max_seqlen_q=self.max_seqlen, max_seqlen_k=self.max_seqlen, route_block_m=w.bm_r,
+            route_block_n=w.bn_r, route_group=w.group, causal=w.causal,
+            softmax_scale=self.softmax_scale, out=self.out, lse=self.lse, debug_s32=debug_s32,
+            debug_head=debug_head, debug_mtile_begin=debug_mtile_begin,
+            debug_mtile_count=debug_mtile_count, stream=stream)
+
+    def step(self, stream=None):
+        self.quantize(stream)
+        self.pack(stream)
+        self.attention(stream)

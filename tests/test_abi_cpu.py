@@ -1,0 +1,146 @@
+"""CPU-side checks of the C ABI: the library loads, exports every declared entry point, the
+ctypes mirror of tilemix_fwd_params matches the C layout, and argument validation rejects bad
+calls before any device work (no GPU is touched by these tests)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from mixed_precision_attention_tilemix_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tilemix.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from mixed_precision_attention_tilemix_amd import build
+        build.build()
+    return B.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?(tilemix_[a-z_0-9]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for n in ("tilemix_quantize_qk", "tilemix_pack_route_mask", "tilemix_prefill_fwd"):
+        assert n in names
+    assert set(names) == set(B.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}\b", out), name
+
+
+def test_params_struct_matches_c_layout(tmp_path):
+    fields = [f for f, _ in B.FwdParams._fields_]
+    src = tmp_path / "layout.c"
+    body = "\n".join(f'  printf("%s %zu\\n", "{f}", offsetof(tilemix_fwd_params, {f}));' for f in fields)
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "tilemix.h"\nint main(void){\n'
+                   '  printf("sizeof %zu\\n", sizeof(tilemix_fwd_params));\n' + body + "\n  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
+    got = dict(line.split() for line in subprocess.check_output([str(exe)], text=True).splitlines())
+    assert int(got["sizeof"]) == ctypes.sizeof(B.FwdParams)
+    for f in fields:
+        assert int(got[f]) == getattr(B.FwdParams, f).offset, f
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
+
+
+def base_params():
+    p = B.FwdParams()
+    p.struct_size = ctypes.sizeof(B.FwdParams)
+    p.batch, p.hq, p.hkv, p.head_dim = 1, 4, 2, 128
+    p.total_q = p.total_k = 256
+    p.max_seqlen_q = p.max_seqlen_k = 256
+    p.cu_seqlens_q = p.cu_seqlens_k = p.cu_mtiles = FAKE
+    p.total_mtiles = 2
+    p.q = p.k = p.v = FAKE
+    p.q_stride_tok, p.q_stride_head = 4 * 128, 128
+    p.k_stride_tok, p.k_stride_head = 2 * 128, 128
+    p.v_stride_tok, p.v_stride_head = 2 * 128, 128
+    p.q8 = p.q_scale = p.k8 = p.k_scale = FAKE
+    p.route_words = FAKE
+    p.words_per_row = 1
+    p.route_block_m, p.route_block_n, p.route_group = 128, 128, 1
+    p.causal = 1
+    p.out = FAKE
+    return p
+
+
+BAD_CASES = [
+    ("struct_size", lambda p: setattr(p, "struct_size", 8), B.TILEMIX_EINVAL),
+    ("head_dim", lambda p: setattr(p, "head_dim", 96), B.TILEMIX_EUNSUPPORTED),
+    ("gqa ratio", lambda p: setattr(p, "hkv", 3), B.TILEMIX_EINVAL),
+    ("route_block_m", lambda p: setattr(p, "route_block_m", 48), B.TILEMIX_EINVAL),
+    ("route_block_n", lambda p: setattr(p, "route_block_n", 96), B.TILEMIX_EINVAL),
+    ("route_group", lambda p: setattr(p, "route_group", 0), B.TILEMIX_EINVAL),
+    ("too many groups", lambda p: setattr(p, "max_seqlen_k", 128 * 65), B.TILEMIX_EINVAL),
+    ("null q8", lambda p: setattr(p, "q8", None), B.TILEMIX_EINVAL),
+    ("null out", lambda p: setattr(p, "out", None), B.TILEMIX_EINVAL),
+    ("kv_int8 with fp16 k", lambda p: setattr(p, "kv_int8", 1), B.TILEMIX_EINVAL),
+    ("fp16 without v", lambda p: setattr(p, "v", None), B.TILEMIX_EINVAL),
+    ("odd stride", lambda p: setattr(p, "q_stride_head", 4), B.TILEMIX_EINVAL),
+    ("misaligned q", lambda p: setattr(p, "q", FAKE + 2), B.TILEMIX_EINVAL),
+    ("out dtype", lambda p: setattr(p, "out_dtype", 7), B.TILEMIX_EINVAL),
+    ("debug range", lambda p: (setattr(p, "debug_s32", FAKE), setattr(p, "debug_head", 9),
+                               setattr(p, "debug_ntiles_max", 2)), B.TILEMIX_EINVAL),
+    ("debug ntiles", lambda p: (setattr(p, "debug_s32", FAKE), setattr(p, "debug_mtile_count", 1),
+                                setattr(p, "debug_ntiles_max", 1)), B.TILEMIX_EINVAL),
+]
+
+
+@pytest.mark.parametrize("name,mutate,status", BAD_CASES, ids=[c[0] for c in BAD_CASES])
+def test_prefill_validation(lib, name, mutate, status):
+    p = base_params()
+    mutate(p)
+    got = lib.tilemix_prefill_fwd(ctypes.byref(p), None)
+    assert got == status, (name, B.last_error())
+    assert B.last_error()
+
+
+def test_prefill_null_params(lib):
+    assert lib.tilemix_prefill_fwd(None, None) == B.TILEMIX_EINVAL
+
+
+def test_quantize_validation(lib):
+    L = lib
+    # unsupported head_dim
+    assert L.tilemix_quantize_qk(FAKE, 8, 2, 256, 128, FAKE, FAKE, None, 0, 0, 0, 0, None, None,
+                                 96, None) == B.TILEMIX_EUNSUPPORTED
+    # input without outputs
+    assert L.tilemix_quantize_qk(FAKE, 8, 2, 256, 128, None, FAKE, None, 0, 0, 0, 0, None, None,
+                                 128, None) == B.TILEMIX_EINVAL
+    # stride not a multiple of 8 elements
+    assert L.tilemix_quantize_qk(FAKE, 8, 2, 256, 129, FAKE, FAKE, None, 0, 0, 0, 0, None, None,
+                                 128, None) == B.TILEMIX_EINVAL
+    # misaligned input
+    assert L.tilemix_quantize_qk(None, 0, 0, 0, 0, None, None, FAKE + 8, 8, 2, 256, 128, FAKE,
+                                 FAKE, 128, None) == B.TILEMIX_EINVAL
+    assert "misaligned" in B.last_error()
+
+
+def test_pack_validation(lib):
+    assert lib.tilemix_pack_route_mask(FAKE, 4, 65, FAKE, 1, None) == B.TILEMIX_EINVAL
+    assert lib.tilemix_pack_route_mask(FAKE, 4, 8, FAKE, 0, None) == B.TILEMIX_EINVAL
+    assert lib.tilemix_pack_route_mask(None, 4, 8, FAKE, 1, None) == B.TILEMIX_EINVAL
+    assert lib.tilemix_pack_route_mask(FAKE, -1, 8, FAKE, 1, None) == B.TILEMIX_EINVAL
+
+
+def test_version(lib):
+    assert B.version() >= 100
