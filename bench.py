@@ -1,0 +1,189 @@
+"""Benchmark of the routed prefill attention hot path on one MI355X.
+
+One step = one pass of the whole hot path on the 32k-token causal GQA workload (32 query /
+8 KV heads, head_dim 128, route tiles 128x128, 4 key tiles per routing bit, the 10% of key
+groups with the largest max|K| on the FP16 path, K with 4 outlier channels x20):
+tilemix_quantize_qk (Q and K) + tilemix_pack_route_mask + tilemix_prefill_fwd, with all
+inputs resident in device memory. TFLOP/s counts 4 * head_dim * Hq flops per legal causal
+(query, key) pair (QK^T and P.V, two flops per multiply-add), divided by the step time.
+
+The JSON line also carries the roofline of the fused kernel (its own launch time from HIP
+events on its stream, against the mixed FP16/INT8 MFMA peak) and the CPU oracle timed on a
+bounded sample of query rows of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP16 = 2516.6   # TFLOP/s, dense FP16 MFMA, MI355X (256 CU x 4096 flop/clk x 2.4 GHz)
+PEAK_INT8 = 5033.2   # TOP/s, dense INT8 MFMA
+PEAK_HBM = 8000.0    # GB/s
+
+WORKLOAD = "gqa32k"
+
+
+def int8_pair_counts(w):
+    """Legal (query, key) pairs per head routed to INT8, summed over heads, from the route map."""
+    rep = w.hq // w.hk
+    n8 = 0
+    cm = w.cu_mtiles
+    for b, L in enumerate(w.seqlens):
+        span = w.bn_r * w.group
+        for m in range(cm[b + 1] - cm[b]):
+            i0, i1 = m * w.bm_r, min(L, (m + 1) * w.bm_r)
+            for gj in range(w.t_mask):
+                j0 = gj * span
+                if j0 >= L:
+                    break
+                j1 = min(L, j0 + span)
+                # pairs (i, j) with i in [i0, i1), j in [j0, j1), j <= i
+                if w.causal:
+                    ii = np.arange(i0, i1)
+                    cnt = int(np.clip(np.minimum(ii + 1, j1) - j0, 0, None).sum())
+                else:
+                    cnt = (i1 - i0) * (j1 - j0)
+                bits = w.route[:, cm[b] + m, gj]
+                n8 += cnt * int(bits.sum()) * rep
+    return n8
+
+
+def cpu_baseline(w, prob, rows):
+    import oracle
+    prep = oracle.prepare(w)
+    t0 = time.perf_counter()
+    out, _, n8, nall = prep.prefill(rows)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.d * nall  # nall counts (row, head, key) legal triples
+    import torch
+    gpu = prob.out[torch.from_numpy(rows).cuda()].cpu().numpy()
+    err = float(np.abs(gpu.astype(np.float64) - out).max())
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": f"{len(rows)} query rows x {w.hq} heads (rows 0, 42, 85 and 127 of every "
+                  f"4th 128-row query tile, {nall} legal pairs), fp64 oracle, {dt:.1f} s",
+        "seconds": dt,
+        "parity_max_abs_err_on_sample": err,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by KV head with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mixed_precision_attention_tilemix_amd import binding, workloads
+    from mixed_precision_attention_tilemix_amd.runner import DeviceProblem
+
+    binding.load()
+    w = workloads.make(args.workload)
+    prob = DeviceProblem(w, out_dtype=torch.float16)
+    stream = torch.cuda.current_stream()
+
+    pairs_per_head = w.legal_pairs()
+    pairs = pairs_per_head * w.hq
+    n8 = int8_pair_counts(w)
+    r = n8 / pairs
+    flops = 4.0 * w.d * pairs
+    # mixed floor: INT8 QK^T at the INT8 peak, FP16 QK^T and all P.V at the FP16 peak
+    t_floor = (2 * w.d * n8) / (PEAK_INT8 * 1e12) + (2 * w.d * (pairs - n8) + 2 * w.d * pairs) / (PEAK_FP16 * 1e12)
+    peak_mixed = flops / t_floor / 1e12
+
+    for _ in range(args.warmup):
+        prob.step()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1, e2 in ev:
+        e0.record(stream)
+        prob.quantize()
+        prob.pack()
+        e1.record(stream)
+        prob.attention()
+        e2.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = float(np.mean([e1.elapsed_time(e2) for _, e1, e2 in ev]))
+    pre_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1, _ in ev]))
+    step_ms = wall * 1e3 / args.steps
+
+    tflops = flops / (step_ms * 1e-3) / 1e12
+    fwd_tflops = flops / (fwd_ms * 1e-3) / 1e12
+    q_bytes = w.total * (w.hq + w.hk) * (w.d * 3 + 4)  # fp16 read + int8 write + fp32 scale
+
+    result = {
+        "metric": "causal prefill attention TFLOPS & % MFMA roofline at L=32k, d=128, GQA",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16+int8 (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": w.batch, "seq_len": w.seqlens[0] if w.batch == 1 else w.total,
+            "hq": w.hq, "hkv": w.hk, "head_dim": w.d, "causal": w.causal,
+            "route_tile": [w.bm_r, w.bn_r], "group": w.group, "policy": w.policy,
+            "int8_pair_fraction": round(r, 4), "out_dtype": "fp16",
+        },
+        "pct_mixed_roofline": round(100 * tflops / peak_mixed, 2),
+        "pct_fp16_roofline": round(100 * tflops / PEAK_FP16, 2),
+        "fwd_ms": round(fwd_ms, 4),
+        "quantize_pack_ms": round(pre_ms, 4),
+        "quantize_gbps": round(q_bytes / (pre_ms * 1e-3) / 1e9, 1),
+        "roofline": {
+            "kernel": "prefill_fwd_kernel<128,NW,false>",
+            "bound": "mfma",
+            "achieved": round(fwd_tflops, 2),
+            "peak": round(peak_mixed, 1),
+            "unit": "TFLOP/s",
+            "frac": round(fwd_tflops / peak_mixed, 4),
+            "traffic": None,
+            "flops_per_launch": flops,
+            "peak_note": f"mixed MFMA peak for INT8 fraction {r:.4f}: INT8 QK^T at {PEAK_INT8}, "
+                         f"FP16 QK^T and P.V at {PEAK_FP16} TFLOP/s",
+        },
+    }
+    if not args.no_cpu_baseline:
+        tiles = list(range(0, w.total_mtiles, 4))
+        if tiles[-1] != w.total_mtiles - 1:
+            tiles.append(w.total_mtiles - 1)
+        rows = []
+        for m in tiles:
+            for off in (0, w.bm_r // 3, (2 * w.bm_r) // 3, w.bm_r - 1):
+                rows.append(m * w.bm_r + off)
+        rows = np.array(sorted(set(x for x in rows if x < w.total)), dtype=np.int64)
+        result["cpu_baseline"] = cpu_baseline(w, prob, rows)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
