@@ -10,7 +10,8 @@
  * P.V (Sections 3.1, 4.1-4.3).
  *
  * Conventions shared by every call:
- *   - All tensor pointers are DEVICE pointers owned by the caller. The library allocates no
+ *   - All tensor pointers are DEVICE pointers owned by the caller, including the workspace of
+ *     tilemix_prefill_fwd (sized by tilemix_prefill_workspace_size). The library allocates no
  *     device memory and keeps no state other than a thread-local error string.
  *   - Calls are asynchronous: they validate the host-side arguments, enqueue kernels on `stream`
  *     (a hipStream_t; NULL = the null stream) and return. The caller synchronises.
@@ -129,7 +130,22 @@ typedef struct tilemix_fwd_params {
    * left untouched, so the caller pre-fills a sentinel. NULL disables it. */
   int32_t* debug_s32;
   int32_t debug_head, debug_mtile_begin, debug_mtile_count, debug_ntiles_max;
+
+  /* Device scratch of at least tilemix_prefill_workspace_size() bytes, 256-byte aligned,
+   * owned by the caller; its contents on entry are irrelevant and on return unspecified.
+   * It holds the transposed V tiles (and, with kv_int8, an fp16 copy of K8). Calls that
+   * share one workspace must not overlap in time. */
+  void* workspace;
+  int64_t workspace_bytes;
 } tilemix_fwd_params;
+
+/*
+ * tilemix_prefill_workspace_size - bytes of device workspace tilemix_prefill_fwd needs for
+ * these parameters (only batch, hkv, head_dim, total_k and kv_int8 are read). Writes *bytes.
+ * Errors: EINVAL for NULL arguments or negative sizes, EUNSUPPORTED for head_dim other than
+ * 64/128.
+ */
+tilemix_status tilemix_prefill_workspace_size(const tilemix_fwd_params* params, int64_t* bytes);
 
 /*
  * tilemix_prefill_fwd - the fused routed attention (Sections 4.1 and 4.3).
@@ -144,10 +160,13 @@ typedef struct tilemix_fwd_params {
  * gets O = 0 and LSE = -inf. Scores, softmax state and the P.V accumulator are fp32; P is
  * rounded to fp16 for the FP16 P.V product.
  *
+ * Implementation: a pre-pass writes V^T tiles (and, with kv_int8, fp16 K) into the workspace,
+ * then the fused kernel runs; both are enqueued on `stream`.
+ *
  * Errors: EINVAL for a NULL required pointer, struct_size mismatch, hq % hkv != 0,
  * route_block_m not a multiple of 32, route_block_n not a multiple of 64, route_group < 1,
- * words_per_row < 1, kv_int8 with non-NULL k/v (or without v8/v_scale), a bad debug range;
- * EUNSUPPORTED for head_dim other than 64/128.
+ * words_per_row < 1, kv_int8 with non-NULL k/v (or without v8/v_scale), a bad debug range,
+ * a NULL, misaligned or too small workspace; EUNSUPPORTED for head_dim other than 64/128.
  */
 tilemix_status tilemix_prefill_fwd(const tilemix_fwd_params* params, void* stream);
 

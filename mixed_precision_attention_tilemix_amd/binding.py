@@ -23,7 +23,7 @@ TILEMIX_OK, TILEMIX_EINVAL, TILEMIX_EUNSUPPORTED, TILEMIX_ELAUNCH = 0, 1, 2, 3
 
 # The entry points declared in include/tilemix.h.
 EXPORTED = ("tilemix_last_error", "tilemix_version", "tilemix_quantize_qk",
-            "tilemix_pack_route_mask", "tilemix_prefill_fwd")
+            "tilemix_pack_route_mask", "tilemix_prefill_workspace_size", "tilemix_prefill_fwd")
 
 
 class TilemixError(RuntimeError):
@@ -62,6 +62,7 @@ class FwdParams(ctypes.Structure):
         ("debug_s32", ctypes.c_void_p),
         ("debug_head", ctypes.c_int32), ("debug_mtile_begin", ctypes.c_int32),
         ("debug_mtile_count", ctypes.c_int32), ("debug_ntiles_max", ctypes.c_int32),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64),
     ]
 
 
@@ -85,6 +86,8 @@ def load(path: Optional[str] = None):
                                       vp, i64, i32, i64, i64, vp, vp, i32, vp]
     L.tilemix_pack_route_mask.restype = ctypes.c_int
     L.tilemix_pack_route_mask.argtypes = [vp, i64, i32, vp, i32, vp]
+    L.tilemix_prefill_workspace_size.restype = ctypes.c_int
+    L.tilemix_prefill_workspace_size.argtypes = [ctypes.POINTER(FwdParams), ctypes.POINTER(ctypes.c_int64)]
     L.tilemix_prefill_fwd.restype = ctypes.c_int
     L.tilemix_prefill_fwd.argtypes = [ctypes.POINTER(FwdParams), vp]
     _lib = L
@@ -148,9 +151,20 @@ def tilemix_pack_route_mask(route: torch.Tensor, words: torch.Tensor, stream=Non
                                           words.shape[-1], _stream(stream)))
 
 
+def tilemix_prefill_workspace_size(*, batch: int, hkv: int, head_dim: int, total_k: int,
+                                   kv_int8: bool) -> int:
+    """Bytes of device workspace tilemix_prefill_fwd needs."""
+    p = FwdParams()
+    p.struct_size = ctypes.sizeof(FwdParams)
+    p.batch, p.hkv, p.head_dim, p.total_k, p.kv_int8 = batch, hkv, head_dim, total_k, int(kv_int8)
+    out = ctypes.c_int64(0)
+    _check(load().tilemix_prefill_workspace_size(ctypes.byref(p), ctypes.byref(out)))
+    return out.value
+
+
 def tilemix_prefill_fwd(*, q, q8, q_scale, k8, k_scale, route_words, cu_seqlens_q, cu_seqlens_k,
                         cu_mtiles, max_seqlen_q: int, max_seqlen_k: int, route_block_m: int,
-                        route_block_n: int, route_group: int, out, k=None, v=None, v8=None,
+                        route_block_n: int, route_group: int, out, workspace, k=None, v=None, v8=None,
                         v_scale=None, causal: bool = True, softmax_scale: float = 0.0, lse=None,
                         debug_s32=None, debug_head: int = 0, debug_mtile_begin: int = 0,
                         debug_mtile_count: int = 0, stream=None) -> None:
@@ -192,4 +206,6 @@ def tilemix_prefill_fwd(*, q, q8, q_scale, k8, k_scale, route_words, cu_seqlens_
     if debug_s32 is not None:
         p.debug_head, p.debug_mtile_begin = debug_head, debug_mtile_begin
         p.debug_mtile_count, p.debug_ntiles_max = debug_mtile_count, debug_s32.shape[1]
+    p.workspace = _ptr(workspace)
+    p.workspace_bytes = workspace.numel() * workspace.element_size()
     _check(load().tilemix_prefill_fwd(ctypes.byref(p), _stream(stream)))

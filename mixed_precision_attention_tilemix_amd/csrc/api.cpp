@@ -9,6 +9,7 @@
 
 #include "../../include/tilemix.h"
 #include "launch.h"
+#include "tile_layout.h"
 
 namespace {
 
@@ -51,6 +52,24 @@ tilemix_status check_quant_group(const char* name, const void* x, int64_t n, int
     return fail(TILEMIX_EINVAL, "quantize_qk: %s pointers misaligned (need 16/8/4 bytes)", name);
   (void)d;
   return TILEMIX_OK;
+}
+
+struct WorkspaceLayout {
+  int64_t vt_tiles;   // V^T tile slots per KV head
+  int64_t vt_bytes;   // bytes of the V^T region
+  int64_t k16_off;    // byte offset of the fp16 K copy (INT8 cache only)
+  int64_t total;      // bytes in all
+};
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+WorkspaceLayout workspace_layout(const tilemix_fwd_params* p) {
+  WorkspaceLayout w{};
+  w.vt_tiles = tilemix::key_tiles_bound(p->total_k, p->batch);
+  w.vt_bytes = round_up(static_cast<int64_t>(p->hkv) * w.vt_tiles * tilemix::kKeyTile * p->head_dim * 2, 256);
+  w.k16_off = w.vt_bytes;
+  w.total = w.vt_bytes + (p->kv_int8 ? round_up(p->total_k * p->hkv * p->head_dim * 2, 256) : 0);
+  return w;
 }
 
 }  // namespace
@@ -99,6 +118,17 @@ tilemix_status tilemix_pack_route_mask(const uint8_t* route, int64_t rows, int32
   return from_hip(tilemix::launch_pack(route, rows, t_mask, words, words_per_row,
                                        static_cast<hipStream_t>(stream)),
                   "pack_route_mask");
+}
+
+tilemix_status tilemix_prefill_workspace_size(const tilemix_fwd_params* p, int64_t* bytes) {
+  if (p == nullptr || bytes == nullptr) return fail(TILEMIX_EINVAL, "prefill_workspace_size: NULL argument");
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(TILEMIX_EUNSUPPORTED, "prefill_workspace_size: head_dim %d (supported: 64, 128)", p->head_dim);
+  if (p->batch < 1 || p->hkv < 1 || p->total_k < 0)
+    return fail(TILEMIX_EINVAL, "prefill_workspace_size: batch=%d hkv=%d total_k=%lld", p->batch, p->hkv,
+                (long long)p->total_k);
+  *bytes = workspace_layout(p).total;
+  return ok();
 }
 
 tilemix_status tilemix_prefill_fwd(const tilemix_fwd_params* p, void* stream) {
@@ -157,6 +187,10 @@ tilemix_status tilemix_prefill_fwd(const tilemix_fwd_params* p, void* stream) {
       return fail(TILEMIX_EINVAL, "prefill_fwd: debug_ntiles_max %d < ceil(max_seqlen_k / route_block_n)",
                   p->debug_ntiles_max);
   }
+  const WorkspaceLayout ws = workspace_layout(p);
+  if (p->workspace == nullptr || !aligned(p->workspace, 256) || p->workspace_bytes < ws.total)
+    return fail(TILEMIX_EINVAL, "prefill_fwd: workspace must be 256-byte aligned and hold %lld bytes (got %lld)",
+                (long long)ws.total, (long long)p->workspace_bytes);
   if (p->total_q == 0 || p->max_seqlen_q == 0) return ok();
 
   const float scale = p->softmax_scale > 0.0f ? p->softmax_scale
@@ -201,9 +235,19 @@ tilemix_status tilemix_prefill_fwd(const tilemix_fwd_params* p, void* stream) {
   a.dump_m0 = p->debug_mtile_begin;
   a.dump_mcount = p->debug_mtile_count;
   a.dump_ntiles = p->debug_ntiles_max;
-  return from_hip(tilemix::launch_prefill(a, p->batch, p->head_dim, p->kv_int8 != 0,
-                                          static_cast<hipStream_t>(stream)),
-                  "prefill_fwd");
+  a.vt_ws = static_cast<_Float16*>(p->workspace);
+  a.vt = a.vt_ws;
+  a.vt_tiles = ws.vt_tiles;
+  a.k16_ws = p->kv_int8 ? reinterpret_cast<_Float16*>(static_cast<char*>(p->workspace) + ws.k16_off) : nullptr;
+  if (p->kv_int8) {  // the FP16-routed tiles read the exact fp16 copy of K8
+    a.k = a.k16_ws;
+    a.k_stride_tok = static_cast<int64_t>(p->hkv) * p->head_dim;
+    a.k_stride_head = p->head_dim;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = tilemix::launch_vt_pack(a, p->batch, p->max_seqlen_k, p->head_dim, p->kv_int8 != 0, s);
+  if (e != hipSuccess) return from_hip(e, "prefill_fwd (V^T pre-pass)");
+  return from_hip(tilemix::launch_prefill(a, p->batch, p->head_dim, p->kv_int8 != 0, s), "prefill_fwd");
 }
 
 }  // extern "C"

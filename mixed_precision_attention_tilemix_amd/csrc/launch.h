@@ -44,7 +44,16 @@ struct FwdArgs {
   float* lse;
   int32_t* dump;
   int32_t dump_head, dump_m0, dump_mcount, dump_ntiles;
+  // workspace written by the V^T pre-pass and read by the fused kernel
+  _Float16* vt_ws;        // [hkv][vt_tiles][D][64] swizzled V^T tiles
+  const _Float16* vt;     // the same, read-only view
+  int64_t vt_tiles;       // tile slots per KV head (>= tiles of all sequences)
+  _Float16* k16_ws;       // INT8 cache only: exact fp16(k8) [total_k, hkv, D]
 };
+
+// V^T tiles (and, with an INT8 cache, fp16 K) into the workspace; must precede launch_prefill.
+hipError_t launch_vt_pack(const FwdArgs& a, int32_t batch, int32_t max_seqlen_k, int32_t head_dim,
+                          bool kv_int8, hipStream_t stream);
 
 hipError_t launch_prefill(const FwdArgs& a, int32_t batch, int32_t head_dim, bool kv_int8,
                           hipStream_t stream);

@@ -4,73 +4,159 @@
 // equation), computes the score tile with the FP16 or the INT8 matrix-core path, and feeds both
 // into one fp32 online-softmax state (Section 3.1 recurrence) before an FP16 P.V.
 //
-// Work decomposition
-//   * one workgroup = NW wavefronts = 32*NW query rows of one query head of one sequence;
-//     grid = (query heads, query tiles in reverse order, sequences): heads vary fastest so that
-//     the heaviest causal tiles of every head start first and the query heads that share a KV
-//     head run side by side.
-//   * each wavefront owns 32 query rows and computes the TRANSPOSED score tile S^T = K Q^T with
-//     32x32 MFMAs, so that the accumulator lands directly in the B-operand layout of the P.V
-//     product O^T += V^T P^T: lane l holds query l%32 and keys 8*(t/4) + 4*(l/32) + t%4 of a
-//     32-key block in accumulator slot t. Row max and row sum need one cross-lane exchange
-//     (lane l with lane l^32).
-//   * the V^T operand is read from the row-major V tile with the gfx950 transposing LDS read
-//     (ds_read_b64_tr_b16), which hands lane i of each 16-lane group the 4 keys of channel i.
-//   * the route bit of a key tile is uniform over the wavefront (route tiles are multiples of
+// Work decomposition and data flow
+//   * one workgroup = 8 wavefronts (two per SIMD) = 256 query rows of one query head of one
+//     sequence; grid = (query heads, query tiles in reverse order, sequences). Heads vary
+//     fastest and are ordered so that consecutive workgroups (which the hardware deals out to
+//     the 8 XCDs in turn) keep the query heads of one KV head on one XCD and its L2, and the
+//     heaviest causal tiles start first.
+//   * each wavefront owns 32 query rows and computes TRANSPOSED score tiles S^T = K Q^T with
+//     32x32 MFMAs, so the accumulator lands in the B-operand layout of O^T += V^T P^T: lane l
+//     holds query l%32. Key rows inside each 32-key block are loaded in a permuted order (bits 2
+//     and 3 of the row index swapped) so that accumulator slots t = 0..7 and 8..15 of lane l
+//     hold 8 CONSECUTIVE keys each: key = 32*kb + 16*(t>>3) + 8*(l>>5) + (t&7). Row max and row
+//     sum need one cross-lane exchange (lane l with lane l^32).
+//   * V^T comes from a pre-pass (vt_pack.hip) that stores every 64-key tile of V transposed and
+//     already swizzled, so the tile is one contiguous block and each P.V operand is a single
+//     16-byte LDS read.
+//   * K / K8 / k_scale / V^T tiles are double-buffered in LDS and filled with direct
+//     global->LDS loads issued one tile ahead; one barrier per tile separates the buffers.
+//     The fp16 Q of the workgroup stays in LDS (read only by FP16-routed tiles), the int8 Q of
+//     each wavefront in registers.
+//   * the route bit of a key tile is uniform over each wavefront (route tiles are multiples of
 //     32 rows and 64 keys), so the FP16 / INT8 choice is a wave-uniform branch.
+//   * softmax in base 2 with the score scale folded into one FMA per element; the running max
+//     is only raised when a row's tile max exceeds it by more than 8 (so P < 256, exact in
+//     fp32 and fp16), which makes the O rescale rare; the row sum is taken from the
+//     fp16-rounded P that also feeds P.V.
 #include "device_types.h"
 #include "launch.h"
+#include "tile_layout.h"
 
 namespace tilemix {
 namespace {
 
-constexpr int BN = 64;  // keys per inner-loop step (one or more steps per route tile column)
+constexpr int BN = kKeyTile;  // keys per inner-loop step
+constexpr int NW = 8;         // wavefronts per workgroup
+constexpr int ROWS_W = 32;    // query rows per wavefront
+constexpr int BM = NW * ROWS_W;
+constexpr float TAU = 8.0f;   // lazy-max threshold (log2 units)
 
-template <int D, bool KV8>
+// LDS layout. Rows are unpadded; 16-byte chunks are XOR-swizzled per row so that each 1 KiB
+// block stays contiguous (one direct wave load) while the rows one operand read touches fall in
+// distinct banks.
+template <int D>
 struct Smem {
-  static constexpr int K16_STRIDE = D * 2 + 32;  // bytes; +32 keeps 4-row groups bank-disjoint
-  static constexpr int K8_STRIDE = D + 16;
-  static constexpr int V16_STRIDE = D * 2 + 32;
-  static constexpr int K16 = 0;
-  static constexpr int K8 = K16 + BN * K16_STRIDE;
-  static constexpr int DK = K8 + BN * K8_STRIDE;
-  static constexpr int V16 = DK + BN * 4;
-  static constexpr int DV = V16 + BN * V16_STRIDE;
-  static constexpr int BYTES = DV + BN * 4;
+  static constexpr int RB16 = D * 2;   // bytes per fp16 row of K / Q
+  static constexpr int RB8 = D;        // bytes per int8 row of K8
+  static constexpr int C16 = RB16 / 16;
+  static constexpr int C8 = RB8 / 16;
+  static constexpr int Q16 = 0;                 // [BM][D] fp16 Q of the workgroup
+  static constexpr int STAGE0 = Q16 + BM * RB16;
+  static constexpr int K16 = 0;                 // offsets inside one stage
+  static constexpr int K8 = K16 + BN * RB16;
+  static constexpr int DK = K8 + BN * RB8;
+  static constexpr int VT = DK + BN * 4;        // [D][BN] fp16 V^T, layout of vt_pack.hip
+  static constexpr int STAGE = VT + D * BN * 2;
+  static constexpr int BYTES = STAGE0 + 2 * STAGE;
+  // The 16 lanes served together read 16 different rows at one chunk index: XOR-ing the chunk
+  // with (row / rows-per-256-bytes) puts them on 16 distinct 16-byte bank groups.
+  __device__ static int f16(int r) { return (r / (256 / RB16)) & (C16 - 1); }
+  __device__ static int f8(int r) { return (r / (256 / RB8)) & (C8 - 1); }
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ half8v cat8(short4v lo, short4v hi) {
-  half4v a = __builtin_bit_cast(half4v, lo);
-  half4v b = __builtin_bit_cast(half4v, hi);
-  return half8v{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#define ONES2 half2v{static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)}
+
+__device__ __forceinline__ half2v pk(float a, float b) {
+  return half2v{static_cast<_Float16>(a), static_cast<_Float16>(b)};  // v_cvt_pk_f16_f32 (RNE)
 }
 
-// 16 int8 values -> 16 fp16 values (exact: |x| <= 127).
-__device__ __forceinline__ void int8x16_to_half(int4v src, half8v* lo, half8v* hi) {
-  const int8_t* s = reinterpret_cast<const int8_t*>(&src);
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One direct global->LDS load per lane: `bytes` from src to lds_block + bytes * lane.
+__device__ __forceinline__ void dma16(const void* src, char* lds_block) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_block, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, char* lds_block) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_block, 4, 0, 0);
+}
+
+// Row index inside a 32-key block that MFMA row r reads: bits 2 and 3 swapped.
+__device__ __forceinline__ int perm32(int r) { return (r & 0x13) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+// Issue the direct loads of the key tile starting at j0 (sequence-local) into stage `buf`.
+// Rows past the sequence end read the last valid row; they are masked before use.
+template <int D>
+__device__ __forceinline__ void stage_issue(const FwdArgs& a, char* buf, const _Float16* vt_tile,
+                                            int w, int lane, int j0, int Lk, int k_begin, int hk,
+                                            bool need16, bool need8, bool need_dk) {
+  using L = Smem<D>;
+  auto key_of = [&](int row) { return static_cast<int64_t>(k_begin + min(j0 + row, Lk - 1)); };
+  constexpr int R16 = 1024 / L::RB16;  // K rows per wave load
+  constexpr int R8 = 1024 / L::RB8;
+  if (need16) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    (*lo)[e] = static_cast<_Float16>(s[e]);
-    (*hi)[e] = static_cast<_Float16>(s[8 + e]);
+    for (int blk = w; blk < BN / R16; blk += NW) {
+      const int row = blk * R16 + lane / L::C16;
+      const int chunk = (lane % L::C16) ^ L::f16(row);
+      dma16(a.k + key_of(row) * a.k_stride_tok + hk * a.k_stride_head + chunk * 8, buf + L::K16 + blk * 1024);
+    }
   }
+  if (need8) {
+#pragma unroll
+    for (int blk = w; blk < BN / R8; blk += NW) {
+      const int row = blk * R8 + lane / L::C8;
+      const int chunk = (lane % L::C8) ^ L::f8(row);
+      dma16(a.k8 + (key_of(row) * a.hkv + hk) * D + chunk * 16, buf + L::K8 + blk * 1024);
+    }
+  }
+  if (need_dk && w == NW - 1)
+    dma4(a.k_scale + static_cast<int64_t>(hk) * a.total_k + key_of(lane), buf + L::DK);
+  const char* vsrc = reinterpret_cast<const char*>(vt_tile);
+#pragma unroll
+  for (int blk = w; blk < D * BN * 2 / 1024; blk += NW) dma16(vsrc + blk * 1024 + lane * 16, buf + L::VT + blk * 1024);
 }
 
-template <int D, int NW, bool KV8>
-__global__ __launch_bounds__(NW * 64) void prefill_fwd_kernel(const FwdArgs a) {
-  using L = Smem<D, KV8>;
-  constexpr int BM = 32 * NW;
-  constexpr int NT = NW * 64;
-  __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+// Route bits of the workgroup's wavefronts for the key tile starting at j0: bit w = route bit of
+// wave w, bit 16+w = wave w computes the tile at all (it has rows in the sequence and not all of
+// them are causally masked).
+__device__ __forceinline__ uint32_t tile_bits(const FwdArgs& a, const uint64_t* words_hk, int mt0,
+                                              int q0, int Lq, int off, int j0) {
+  const int gj = (j0 / a.bn_r) / a.group;
+  uint32_t bits = 0;
+#pragma unroll
+  for (int wv = 0; wv < NW; ++wv) {
+    const int qa = q0 + ROWS_W * wv;
+    const int qlast = min(qa + ROWS_W - 1, Lq - 1);
+    const bool act = qa < Lq && !(a.causal && j0 > qlast + off);
+    if (act) {
+      const uint64_t word = words_hk[static_cast<int64_t>(mt0 + qa / a.bm_r) * a.wpr + (gj >> 6)];
+      bits |= (static_cast<uint32_t>((word >> (gj & 63)) & 1u) << wv) | (1u << (16 + wv));
+    }
+  }
+  return bits;
+}
+
+__device__ __forceinline__ bool any_fp16(uint32_t bits) { return ((bits >> 16) & ~bits & 0xffu) != 0; }
+__device__ __forceinline__ bool any_int8(uint32_t bits) { return ((bits >> 16) & bits & 0xffu) != 0; }
+
+template <int D, bool KV8>
+__global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a) {
+  using L = Smem<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int hl = lane >> 5;       // which half of the wave (key sub-rows of the C layout)
-  const int r32 = lane & 31;      // query row within the wave / key row within a block
+  const int hl = lane >> 5;   // half of the wave: selects 8 of the 16 keys of a k-step
+  const int r32 = lane & 31;  // query row of this lane within the wave
 
-  const int h = blockIdx.x;
+  // XCD-friendly head order: consecutive workgroups cycle through the KV heads first
+  const int x = blockIdx.x;
+  const int grp = a.hq / a.hkv;
+  const int h = grp * (x % a.hkv) + x / a.hkv;
   const int b = blockIdx.z;
   const int n_ct = (a.max_seqlen_q + BM - 1) / BM;
   const int c = n_ct - 1 - static_cast<int>(blockIdx.y);
@@ -81,44 +167,57 @@ __global__ __launch_bounds__(NW * 64) void prefill_fwd_kernel(const FwdArgs a) {
   const int q0 = c * BM;
   if (q0 >= Lq) return;  // uniform over the workgroup
 
-  const int hk = h / (a.hq / a.hkv);
+  const int hk = h / grp;
   const int off = Lk - Lq;  // bottom-right causal alignment
   const int q_last = min(q0 + BM, Lq) - 1;
   const int key_end = a.causal ? min(Lk, q_last + off + 1) : Lk;
   const int n_tiles = key_end > 0 ? (key_end + BN - 1) / BN : 0;
 
-  const int qa = q0 + 32 * w;          // first query row of this wave
-  const bool wave_active = qa < Lq;
-  const int my_q = qa + r32;           // this lane's query row (local to the sequence)
+  const int qa = q0 + ROWS_W * w;  // first query row of this wave
+  const int my_q = qa + r32;
   const bool row_valid = my_q < Lq;
+  const uint64_t* words_hk = a.words + static_cast<int64_t>(hk) * a.total_mtiles * a.wpr;
+  const int mt0 = a.cu_mtiles[b];
+  char* const stage0 = smem + L::STAGE0;
+  const _Float16* vt_head =
+      a.vt + (static_cast<int64_t>(hk) * a.vt_tiles + key_tiles_before(a.cu_k, b)) * (D * BN);
 
-  // ---- resident query fragments: B operands of S^T = K Q^T
-  half8v qf[D / 16];
+  // ---- per-lane LDS offsets of the MFMA operands (kb / dblk / kk steps are immediates)
+  const int kr = perm32(r32);  // K row this lane feeds to the MFMA
+  int koff16[D / 16], qoff16[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    koff16[ks] = kr * L::RB16 + 16 * ((2 * ks + hl) ^ L::f16(kr));
+    qoff16[ks] = (ROWS_W * w + r32) * L::RB16 + 16 * ((2 * ks + hl) ^ L::f16(ROWS_W * w + r32));
+  }
+  int koff8[D / 32];
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) koff8[ks] = kr * L::RB8 + 16 * ((2 * ks + hl) ^ L::f8(kr));
+  int voff[BN / 16];  // V^T row r32 (+32*dblk), chunk 2*kk + hl
+#pragma unroll
+  for (int kk = 0; kk < BN / 16; ++kk) voff[kk] = r32 * (BN * 2) + 16 * ((2 * kk + hl) ^ vt_swizzle(r32));
+
+  // ---- resident queries: fp16 Q of the workgroup in LDS, this wave's int8 Q in registers
+  for (int ch = tid; ch < BM * L::C16; ch += NW * 64) {
+    const int row = ch / L::C16, col = ch % L::C16;
+    int4v val = {};
+    if (q0 + row < Lq)
+      val = *reinterpret_cast<const int4v*>(a.q + (q_begin + q0 + row) * a.q_stride_tok +
+                                            static_cast<int64_t>(h) * a.q_stride_head + col * 8);
+    *reinterpret_cast<int4v*>(smem + L::Q16 + row * L::RB16 + 16 * (col ^ L::f16(row))) = val;
+  }
   int4v q8f[D / 32];
-  float cq = 0.0f;  // q_scale * softmax_scale * log2(e)
+  float cq = 1e-30f;  // q_scale * softmax_scale * log2(e), floored so that 0 * -inf cannot occur
   if (row_valid) {
     const int64_t tq = q_begin + my_q;
-    const _Float16* qp = a.q + tq * a.q_stride_tok + static_cast<int64_t>(h) * a.q_stride_head;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-      qf[ks] = *reinterpret_cast<const half8v*>(qp + 16 * ks + 8 * hl);
     const int8_t* q8p = a.q8 + (tq * a.hq + h) * D;
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks)
-      q8f[ks] = *reinterpret_cast<const int4v*>(q8p + 32 * ks + 16 * hl);
-    cq = a.q_scale[static_cast<int64_t>(h) * a.total_q + tq] * a.scale_log2;
+    for (int ks = 0; ks < D / 32; ++ks) q8f[ks] = *reinterpret_cast<const int4v*>(q8p + 32 * ks + 16 * hl);
+    cq = fmaxf(a.q_scale[static_cast<int64_t>(h) * a.total_q + tq] * a.scale_log2, 1e-30f);
   } else {
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) qf[ks] = half8v{};
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) q8f[ks] = int4v{};
   }
-
-  const uint64_t* words_hk = a.words + static_cast<int64_t>(hk) * a.total_mtiles * a.wpr;
-  const int mt0 = a.cu_mtiles[b];
-  const int my_route_row = mt0 + qa / a.bm_r;
-  const bool dump_wave = a.dump != nullptr && h == a.dump_head && wave_active &&
-                         my_route_row >= a.dump_m0 && my_route_row < a.dump_m0 + a.dump_mcount;
 
   float16v o[D / 32];
 #pragma unroll
@@ -126,229 +225,150 @@ __global__ __launch_bounds__(NW * 64) void prefill_fwd_kernel(const FwdArgs a) {
   float m_i = -INFINITY;  // running max, log2 domain
   float l_i = 0.0f;       // running normaliser
 
-  const int G16 = lane >> 4, s16 = lane & 15;  // transposing-read lane coordinates
+  const int my_rr = mt0 + qa / a.bm_r;
+  const bool dump_me = a.dump != nullptr && h == a.dump_head && qa < Lq && my_rr >= a.dump_m0 &&
+                       my_rr < a.dump_m0 + a.dump_mcount;
+
+  // ---- prologue: tile 0 into stage 0
+  uint32_t bits_next = n_tiles > 0 ? tile_bits(a, words_hk, mt0, q0, Lq, off, 0) : 0;
+  if (n_tiles > 0)
+    stage_issue<D>(a, stage0, vt_head, w, lane, 0, Lk, k_begin, hk, any_fp16(bits_next),
+                   any_int8(bits_next), any_int8(bits_next) || KV8);
+  __syncthreads();
 
   for (int n = 0; n < n_tiles; ++n) {
     const int j0 = n * BN;
-    const int gj = (j0 / a.bn_r) / a.group;
-    // route bits of every wave of the workgroup for this key tile
-    bool need16 = false, need8 = false, my_compute = false;
-    int my_bit = 0;
-#pragma unroll
-    for (int wv = 0; wv < NW; ++wv) {
-      const int qa_w = q0 + 32 * wv;
-      if (qa_w >= Lq) continue;
-      const int qlast_w = min(qa_w + 31, Lq - 1);
-      if (a.causal && j0 > qlast_w + off) continue;  // tile fully masked for that wave
-      const int rr = mt0 + qa_w / a.bm_r;
-      const uint64_t word = words_hk[static_cast<int64_t>(rr) * a.wpr + (gj >> 6)];
-      const int bit = static_cast<int>((word >> (gj & 63)) & 1u);
-      need8 |= bit != 0;
-      need16 |= bit == 0;
-      if (wv == w) {
-        my_compute = true;
-        my_bit = bit;
-      }
+    const uint32_t bits = bits_next;
+    const char* cur = stage0 + (n & 1) * L::STAGE;
+    if (n + 1 < n_tiles) {
+      bits_next = tile_bits(a, words_hk, mt0, q0, Lq, off, j0 + BN);
+      stage_issue<D>(a, stage0 + ((n + 1) & 1) * L::STAGE, vt_head + (n + 1) * (D * BN), w, lane,
+                     j0 + BN, Lk, k_begin, hk, any_fp16(bits_next), any_int8(bits_next),
+                     any_int8(bits_next) || KV8);
     }
 
-    __syncthreads();  // the previous tile's readers are done with LDS
-
-    // ---- stage the key/value tile into LDS (zero rows past the sequence end)
-    if (!KV8) {
-      if (need16) {
-        for (int ch = tid; ch < BN * (D / 8); ch += NT) {
-          const int row = ch / (D / 8), col = ch % (D / 8);
-          const int key = j0 + row;
-          half8v val = {};
-          if (key < Lk)
-            val = *reinterpret_cast<const half8v*>(a.k + (k_begin + key) * a.k_stride_tok +
-                                                   hk * a.k_stride_head + col * 8);
-          *reinterpret_cast<half8v*>(smem + L::K16 + row * L::K16_STRIDE + col * 16) = val;
-        }
-      }
-      if (need8) {
-        for (int ch = tid; ch < BN * (D / 16); ch += NT) {
-          const int row = ch / (D / 16), col = ch % (D / 16);
-          const int key = j0 + row;
-          int4v val = {};
-          if (key < Lk)
-            val = *reinterpret_cast<const int4v*>(a.k8 + ((k_begin + key) * static_cast<int64_t>(a.hkv) + hk) * D + col * 16);
-          *reinterpret_cast<int4v*>(smem + L::K8 + row * L::K8_STRIDE + col * 16) = val;
-        }
-        for (int row = tid; row < BN; row += NT) {
-          const int key = j0 + row;
-          reinterpret_cast<float*>(smem + L::DK)[row] =
-              key < Lk ? a.k_scale[static_cast<int64_t>(hk) * a.total_k + k_begin + key] : 0.0f;
-        }
-      }
-      for (int ch = tid; ch < BN * (D / 8); ch += NT) {
-        const int row = ch / (D / 8), col = ch % (D / 8);
-        const int key = j0 + row;
-        half8v val = {};
-        if (key < Lk)
-          val = *reinterpret_cast<const half8v*>(a.v + (k_begin + key) * a.v_stride_tok +
-                                                 hk * a.v_stride_head + col * 8);
-        *reinterpret_cast<half8v*>(smem + L::V16 + row * L::V16_STRIDE + col * 16) = val;
-      }
-    } else {
-      // INT8 cache: K8 feeds the INT8 path directly and, converted exactly to fp16, the FP16
-      // path; V8 is converted exactly to fp16 and its scale is applied to P.
-      for (int ch = tid; ch < BN * (D / 16); ch += NT) {
-        const int row = ch / (D / 16), col = ch % (D / 16);
-        const int key = j0 + row;
-        int4v kv = {}, vv = {};
-        if (key < Lk) {
-          const int64_t base = ((k_begin + key) * static_cast<int64_t>(a.hkv) + hk) * D + col * 16;
-          kv = *reinterpret_cast<const int4v*>(a.k8 + base);
-          vv = *reinterpret_cast<const int4v*>(a.v8 + base);
-        }
-        if (need8) *reinterpret_cast<int4v*>(smem + L::K8 + row * L::K8_STRIDE + col * 16) = kv;
-        if (need16) {
-          half8v lo, hi;
-          int8x16_to_half(kv, &lo, &hi);
-          *reinterpret_cast<half8v*>(smem + L::K16 + row * L::K16_STRIDE + col * 32) = lo;
-          *reinterpret_cast<half8v*>(smem + L::K16 + row * L::K16_STRIDE + col * 32 + 16) = hi;
-        }
-        half8v lo, hi;
-        int8x16_to_half(vv, &lo, &hi);
-        *reinterpret_cast<half8v*>(smem + L::V16 + row * L::V16_STRIDE + col * 32) = lo;
-        *reinterpret_cast<half8v*>(smem + L::V16 + row * L::V16_STRIDE + col * 32 + 16) = hi;
-      }
-      for (int row = tid; row < BN; row += NT) {
-        const int key = j0 + row;
-        const int64_t si = static_cast<int64_t>(hk) * a.total_k + k_begin + key;
-        reinterpret_cast<float*>(smem + L::DK)[row] = key < Lk ? a.k_scale[si] : 0.0f;
-        reinterpret_cast<float*>(smem + L::DV)[row] = key < Lk ? a.v_scale[si] : 0.0f;
-      }
-    }
-
-    __syncthreads();
-
-    if (!my_compute) continue;
-
-    // ---- score tile S^T (64 keys x 32 queries) in the log2 domain
-    float s[2][16];
-    const float* dk = reinterpret_cast<const float*>(smem + L::DK);
-    if (my_bit) {
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        int16v acc = {};
+    if ((bits >> (16 + w)) & 1u) {
+      const float* dk = reinterpret_cast<const float*>(cur + L::DK);
+      float16v s[2];  // [key block], pre-softmax units
+      float cs;
+      if ((bits >> w) & 1u) {
+        // ---- INT8 path: int32 accumulation, then per-key scale (per-query scale folded in cs)
+        int16v acc[2] = {};
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks) {
-          const int4v av = *reinterpret_cast<const int4v*>(
-              smem + L::K8 + (blk * 32 + r32) * L::K8_STRIDE + 32 * ks + 16 * hl);
-          acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, q8f[ks], acc, 0, 0, 0);
+          const int4v k0 = *reinterpret_cast<const int4v*>(cur + L::K8 + koff8[ks]);
+          const int4v k1 = *reinterpret_cast<const int4v*>(cur + L::K8 + 32 * L::RB8 + koff8[ks]);
+          acc[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(k0, q8f[ks], acc[0], 0, 0, 0);
+          acc[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1, q8f[ks], acc[1], 0, 0, 0);
         }
-        if (dump_wave && row_valid) {
-          const int i_in = my_q % a.bm_r;
+        if (dump_me && row_valid) {
+          const int64_t rbase = static_cast<int64_t>(my_rr - a.dump_m0) * a.dump_ntiles;
 #pragma unroll
-          for (int t = 0; t < 16; ++t) {
-            const int key = j0 + blk * 32 + 8 * (t / 4) + 4 * hl + (t % 4);
-            if (key < Lk) {
-              const int64_t idx =
-                  ((static_cast<int64_t>(my_route_row - a.dump_m0) * a.dump_ntiles + key / a.bn_r) *
-                       a.bm_r + i_in) * a.bn_r + key % a.bn_r;
-              a.dump[idx] = acc[t];
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+              const int key = j0 + 32 * kb + 16 * (t >> 3) + 8 * hl + (t & 7);
+              if (key < Lk)
+                a.dump[((rbase + key / a.bn_r) * a.bm_r + my_q % a.bm_r) * a.bn_r + key % a.bn_r] = acc[kb][t];
+            }
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int g8 = 0; g8 < 2; ++g8) {
+            const float4v d0 = *reinterpret_cast<const float4v*>(dk + 32 * kb + 16 * g8 + 8 * hl);
+            const float4v d1 = *reinterpret_cast<const float4v*>(dk + 32 * kb + 16 * g8 + 8 * hl + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              s[kb][8 * g8 + e] = static_cast<float>(acc[kb][8 * g8 + e]) * d0[e];
+              s[kb][8 * g8 + 4 + e] = static_cast<float>(acc[kb][8 * g8 + 4 + e]) * d1[e];
             }
           }
-        }
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const float4v dk4 = *reinterpret_cast<const float4v*>(dk + blk * 32 + 8 * g4 + 4 * hl);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            s[blk][4 * g4 + e] = static_cast<float>(acc[4 * g4 + e]) * dk4[e] * cq;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        float16v acc = {};
+        cs = cq;
+      } else {
+        // ---- FP16 path
+        float16v acc[2] = {};
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
-          const half8v av = *reinterpret_cast<const half8v*>(
-              smem + L::K16 + (blk * 32 + r32) * L::K16_STRIDE + (16 * ks + 8 * hl) * 2);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, qf[ks], acc, 0, 0, 0);
+          const half8v qv = *reinterpret_cast<const half8v*>(smem + L::Q16 + qoff16[ks]);
+          const half8v k0 = *reinterpret_cast<const half8v*>(cur + L::K16 + koff16[ks]);
+          const half8v k1 = *reinterpret_cast<const half8v*>(cur + L::K16 + 32 * L::RB16 + koff16[ks]);
+          acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0, qv, acc[0], 0, 0, 0);
+          acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1, qv, acc[1], 0, 0, 0);
         }
         if (KV8) {
+          // K of the INT8 cache enters the FP16 path as exact fp16(k8): apply its scale here
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const float4v dk4 = *reinterpret_cast<const float4v*>(dk + blk * 32 + 8 * g4 + 4 * hl);
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) s[blk][4 * g4 + e] = acc[4 * g4 + e] * (dk4[e] * a.scale_log2);
-          }
+            for (int g8 = 0; g8 < 2; ++g8) {
+              const float4v d0 = *reinterpret_cast<const float4v*>(dk + 32 * kb + 16 * g8 + 8 * hl);
+              const float4v d1 = *reinterpret_cast<const float4v*>(dk + 32 * kb + 16 * g8 + 8 * hl + 4);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                s[kb][8 * g8 + e] = acc[kb][8 * g8 + e] * d0[e];
+                s[kb][8 * g8 + 4 + e] = acc[kb][8 * g8 + 4 + e] * d1[e];
+              }
+            }
         } else {
+          s[0] = acc[0];
+          s[1] = acc[1];
+        }
+        cs = a.scale_log2;  // fp16 Q is not quantized: only the softmax scale remains
+      }
+
+      // ---- legality mask (diagonal and tail tiles only)
+      if ((j0 + BN > Lk) || (a.causal && j0 + BN - 1 > qa + off)) {
 #pragma unroll
-          for (int t = 0; t < 16; ++t) s[blk][t] = acc[t] * a.scale_log2;
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int t = 0; t < 16; ++t) {
+            const int key = j0 + 32 * kb + 16 * (t >> 3) + 8 * hl + (t & 7);
+            const bool legal = key < Lk && (!a.causal || key <= my_q + off);
+            if (!legal) s[kb][t] = -INFINITY;
+          }
+      }
+
+      // ---- online softmax (Section 3.1 recurrence), base 2, lazy max
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int t = 0; t < 16; t += 2) mx = fmaxf(fmaxf(mx, s[kb][t]), s[kb][t + 1]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float tile_max = mx * cs;  // cs > 0
+      if (__any(tile_max > m_i + TAU)) {
+        const float m_new = tile_max > m_i + TAU ? tile_max : m_i;
+        const float alpha = m_new > m_i ? fast_exp2(m_i - m_new) : 1.0f;
+        l_i *= alpha;
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) o[i] *= alpha;
+        m_i = m_new;
+      }
+      const float m_use = m_i == -INFINITY ? 0.0f : m_i;
+
+      // ---- P = exp2(s*c - m) in fp16, O^T += V^T P^T (16 keys per MFMA step)
+      float rs = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < BN / 16; ++kk) {
+        half8v pb;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const half2v h2 = pk(fast_exp2(fmaf(s[kk >> 1][8 * (kk & 1) + e], cs, -m_use)),
+                               fast_exp2(fmaf(s[kk >> 1][8 * (kk & 1) + e + 1], cs, -m_use)));
+          pb[e] = h2[0];
+          pb[e + 1] = h2[1];
+          rs = __builtin_amdgcn_fdot2(h2, ONES2, rs, false);
+        }
+#pragma unroll
+        for (int dblk = 0; dblk < D / 32; ++dblk) {
+          const half8v vf = *reinterpret_cast<const half8v*>(cur + L::VT + dblk * 32 * (BN * 2) + voff[kk]);
+          o[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pb, o[dblk], 0, 0, 0);
         }
       }
+      l_i += rs + __shfl_xor(rs, 32);
     }
-
-    // ---- legality mask (diagonal and tail tiles only)
-    const bool need_mask = (j0 + BN > Lk) || (a.causal && j0 + BN - 1 > qa + off);
-    if (need_mask) {
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const int key = j0 + blk * 32 + 8 * (t / 4) + 4 * hl + (t % 4);
-          const bool legal = key < Lk && (!a.causal || key <= my_q + off);
-          if (!legal) s[blk][t] = -INFINITY;
-        }
-    }
-
-    // ---- online softmax update (Section 3.1 recurrence, fp32 state, base-2 exponentials)
-    float mx = -INFINITY;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int t = 0; t < 16; ++t) mx = fmaxf(mx, s[blk][t]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_i, mx);
-    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-    const float alpha = fast_exp2(m_i - m_use);
-    float rs = 0.0f;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        s[blk][t] = fast_exp2(s[blk][t] - m_use);
-        rs += s[blk][t];
-      }
-    rs += __shfl_xor(rs, 32);
-    l_i = l_i * alpha + rs;
-    m_i = m_new;
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) o[i] *= alpha;
-
-    if (KV8) {
-      const float* dv = reinterpret_cast<const float*>(smem + L::DV);
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const float4v dv4 = *reinterpret_cast<const float4v*>(dv + blk * 32 + 8 * g4 + 4 * hl);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) s[blk][4 * g4 + e] *= dv4[e];
-        }
-    }
-
-    // ---- O^T += V^T P^T, 16 keys per MFMA
-#pragma unroll
-    for (int kk = 0; kk < BN / 16; ++kk) {
-      half8v pb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = static_cast<_Float16>(s[kk / 2][8 * (kk % 2) + e]);
-      const int row0 = 16 * kk + 4 * (G16 >> 1) + (s16 >> 2);
-#pragma unroll
-      for (int dblk = 0; dblk < D / 32; ++dblk) {
-        const int col = dblk * 32 + 16 * (G16 & 1) + 4 * (s16 & 3);
-        const char* p0 = smem + L::V16 + row0 * L::V16_STRIDE + col * 2;
-        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(p0));
-        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(p0 + 8 * L::V16_STRIDE));
-        o[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cat8(lo, hi), pb, o[dblk], 0, 0, 0);
-      }
-    }
+    __syncthreads();  // waits for this thread's direct loads, then for everyone's
   }
 
   // ---- epilogue: O = O^T / l, LSE = (m + log2 l) * ln 2
@@ -383,13 +403,12 @@ __global__ __launch_bounds__(NW * 64) void prefill_fwd_kernel(const FwdArgs a) {
         l_i > 0.0f ? (m_i + log2f(l_i)) * 0.69314718055994531f : -INFINITY;
 }
 
-template <int D, int NW, bool KV8>
+template <int D, bool KV8>
 hipError_t launch_t(const FwdArgs& a, int32_t batch, hipStream_t stream) {
-  constexpr int BM = 32 * NW;
   const int n_ct = (a.max_seqlen_q + BM - 1) / BM;
   if (n_ct == 0 || batch == 0) return hipSuccess;
   dim3 grid(static_cast<unsigned>(a.hq), static_cast<unsigned>(n_ct), static_cast<unsigned>(batch));
-  prefill_fwd_kernel<D, NW, KV8><<<grid, dim3(NW * 64), 0, stream>>>(a);
+  prefill_fwd_kernel<D, KV8><<<grid, dim3(NW * 64), 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -397,10 +416,9 @@ hipError_t launch_t(const FwdArgs& a, int32_t batch, hipStream_t stream) {
 
 hipError_t launch_prefill(const FwdArgs& a, int32_t batch, int32_t head_dim, bool kv_int8,
                           hipStream_t stream) {
-  constexpr int NW = 4;
   if (head_dim == 128)
-    return kv_int8 ? launch_t<128, NW, true>(a, batch, stream) : launch_t<128, NW, false>(a, batch, stream);
-  return kv_int8 ? launch_t<64, NW, true>(a, batch, stream) : launch_t<64, NW, false>(a, batch, stream);
+    return kv_int8 ? launch_t<128, true>(a, batch, stream) : launch_t<128, false>(a, batch, stream);
+  return kv_int8 ? launch_t<64, true>(a, batch, stream) : launch_t<64, false>(a, batch, stream);
 }
 
 }  // namespace tilemix

@@ -37,6 +37,9 @@ class DeviceProblem:
         self.lse = torch.empty((hq, T), dtype=torch.float32, device=dev) if with_lse else None
         self.softmax_scale = softmax_scale
         self.max_seqlen = max(w.seqlens) if w.seqlens else 0
+        ws_bytes = B.tilemix_prefill_workspace_size(batch=w.batch, hkv=hk, head_dim=d, total_k=T,
+                                                    kv_int8=w.kv_int8)
+        self.workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
         if w.kv_int8:
             k = torch.from_numpy(w.k).to(dev)
             v = torch.from_numpy(w.v).to(dev)
@@ -71,7 +74,8 @@ class DeviceProblem:
             cu_seqlens_q=self.cu, cu_seqlens_k=self.cu, cu_mtiles=self.cu_mtiles,
             max_seqlen_q=self.max_seqlen, max_seqlen_k=self.max_seqlen, route_block_m=w.bm_r,
             route_block_n=w.bn_r, route_group=w.group, causal=w.causal,
-            softmax_scale=self.softmax_scale, out=self.out, lse=self.lse, debug_s32=debug_s32,
+            softmax_scale=self.softmax_scale, out=self.out, lse=self.lse, workspace=self.workspace,
+            debug_s32=debug_s32,
             debug_head=debug_head, debug_mtile_begin=debug_mtile_begin,
             debug_mtile_count=debug_mtile_count, stream=stream)
 

@@ -80,6 +80,8 @@ def base_params():
     p.route_block_m, p.route_block_n, p.route_group = 128, 128, 1
     p.causal = 1
     p.out = FAKE
+    p.workspace = FAKE
+    p.workspace_bytes = 1 << 40
     return p
 
 
@@ -98,6 +100,9 @@ BAD_CASES = [
     ("odd stride", lambda p: setattr(p, "q_stride_head", 4), B.TILEMIX_EINVAL),
     ("misaligned q", lambda p: setattr(p, "q", FAKE + 2), B.TILEMIX_EINVAL),
     ("out dtype", lambda p: setattr(p, "out_dtype", 7), B.TILEMIX_EINVAL),
+    ("null workspace", lambda p: setattr(p, "workspace", None), B.TILEMIX_EINVAL),
+    ("small workspace", lambda p: setattr(p, "workspace_bytes", 1024), B.TILEMIX_EINVAL),
+    ("misaligned workspace", lambda p: setattr(p, "workspace", FAKE + 16), B.TILEMIX_EINVAL),
     ("debug range", lambda p: (setattr(p, "debug_s32", FAKE), setattr(p, "debug_head", 9),
                                setattr(p, "debug_ntiles_max", 2)), B.TILEMIX_EINVAL),
     ("debug ntiles", lambda p: (setattr(p, "debug_s32", FAKE), setattr(p, "debug_mtile_count", 1),
@@ -140,6 +145,20 @@ def test_pack_validation(lib):
     assert lib.tilemix_pack_route_mask(FAKE, 4, 8, FAKE, 0, None) == B.TILEMIX_EINVAL
     assert lib.tilemix_pack_route_mask(None, 4, 8, FAKE, 1, None) == B.TILEMIX_EINVAL
     assert lib.tilemix_pack_route_mask(FAKE, -1, 8, FAKE, 1, None) == B.TILEMIX_EINVAL
+
+
+def test_workspace_size(lib):
+    p = base_params()
+    n = ctypes.c_int64(0)
+    assert lib.tilemix_prefill_workspace_size(ctypes.byref(p), ctypes.byref(n)) == B.TILEMIX_OK
+    # V^T tiles: hkv * (ceil(total_k / 64) + batch) tiles of 64 x head_dim fp16
+    assert n.value == 2 * (256 // 64 + 1) * 64 * 128 * 2
+    p.kv_int8 = 1
+    assert lib.tilemix_prefill_workspace_size(ctypes.byref(p), ctypes.byref(n)) == B.TILEMIX_OK
+    assert n.value == 2 * 5 * 64 * 128 * 2 + 256 * 2 * 128 * 2
+    p.head_dim = 80
+    assert lib.tilemix_prefill_workspace_size(ctypes.byref(p), ctypes.byref(n)) == B.TILEMIX_EUNSUPPORTED
+    assert lib.tilemix_prefill_workspace_size(None, ctypes.byref(n)) == B.TILEMIX_EINVAL
 
 
 def test_version(lib):

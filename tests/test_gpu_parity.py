@@ -210,7 +210,9 @@ def test_bottom_right_causal_unequal_lengths():
     B.tilemix_pack_route_mask(t(R).view(-1, R.shape[-1]), words.view(-1, 1))
     out = torch.empty((Lq, hq, d), dtype=torch.float32, device="cuda")
     lse = torch.empty((hq, Lq), dtype=torch.float32, device="cuda")
-    B.tilemix_prefill_fwd(q=dq, k=dk, v=dv, q8=g8, q_scale=gs, k8=gk8, k_scale=gks, route_words=words,
+    ws = torch.empty(B.tilemix_prefill_workspace_size(batch=1, hkv=hk, head_dim=d, total_k=Lk, kv_int8=False),
+                     dtype=torch.uint8, device="cuda")
+    B.tilemix_prefill_fwd(workspace=ws, q=dq, k=dk, v=dv, q8=g8, q_scale=gs, k8=gk8, k_scale=gks, route_words=words,
                           cu_seqlens_q=t(cu_q), cu_seqlens_k=t(cu_k), cu_mtiles=t(cu_m),
                           max_seqlen_q=Lq, max_seqlen_k=Lk, route_block_m=bm, route_block_n=bn,
                           route_group=1, causal=True, out=out, lse=lse)
