@@ -57,6 +57,7 @@ tilemix_status check_quant_group(const char* name, const void* x, int64_t n, int
 struct WorkspaceLayout {
   int64_t vt_tiles;   // V^T tile slots per KV head
   int64_t vt_bytes;   // bytes of the V^T region
+  int64_t ks_off;     // byte offset of the per-key score factors
   int64_t k16_off;    // byte offset of the fp16 K copy (INT8 cache only)
   int64_t total;      // bytes in all
 };
@@ -67,8 +68,9 @@ WorkspaceLayout workspace_layout(const tilemix_fwd_params* p) {
   WorkspaceLayout w{};
   w.vt_tiles = tilemix::key_tiles_bound(p->total_k, p->batch);
   w.vt_bytes = round_up(static_cast<int64_t>(p->hkv) * w.vt_tiles * tilemix::kKeyTile * p->head_dim * 2, 256);
-  w.k16_off = w.vt_bytes;
-  w.total = w.vt_bytes + (p->kv_int8 ? round_up(p->total_k * p->hkv * p->head_dim * 2, 256) : 0);
+  w.ks_off = w.vt_bytes;
+  w.k16_off = w.ks_off + round_up(static_cast<int64_t>(p->hkv) * w.vt_tiles * 2 * tilemix::kKeyTile * 4, 256);
+  w.total = w.k16_off + (p->kv_int8 ? round_up(p->total_k * p->hkv * p->head_dim * 2, 256) : 0);
   return w;
 }
 
@@ -238,6 +240,8 @@ tilemix_status tilemix_prefill_fwd(const tilemix_fwd_params* p, void* stream) {
   a.vt_ws = static_cast<_Float16*>(p->workspace);
   a.vt = a.vt_ws;
   a.vt_tiles = ws.vt_tiles;
+  a.ks_ws = reinterpret_cast<float*>(static_cast<char*>(p->workspace) + ws.ks_off);
+  a.ks = a.ks_ws;
   a.k16_ws = p->kv_int8 ? reinterpret_cast<_Float16*>(static_cast<char*>(p->workspace) + ws.k16_off) : nullptr;
   if (p->kv_int8) {  // the FP16-routed tiles read the exact fp16 copy of K8
     a.k = a.k16_ws;

@@ -48,6 +48,8 @@ struct FwdArgs {
   _Float16* vt_ws;        // [hkv][vt_tiles][D][64] swizzled V^T tiles
   const _Float16* vt;     // the same, read-only view
   int64_t vt_tiles;       // tile slots per KV head (>= tiles of all sequences)
+  float* ks_ws;           // [hkv][vt_tiles][2][64] per-key score factors dk' and -1.5*2^23*dk'
+  const float* ks;        // the same, read-only view
   _Float16* k16_ws;       // INT8 cache only: exact fp16(k8) [total_k, hkv, D]
 };
 

@@ -4,7 +4,7 @@
 // equation), computes the score tile with the FP16 or the INT8 matrix-core path, and feeds both
 // into one fp32 online-softmax state (Section 3.1 recurrence) before an FP16 P.V.
 //
-// Work decomposition and data flow
+// Work decomposition
 //   * one workgroup = 8 wavefronts (two per SIMD) = 256 query rows of one query head of one
 //     sequence; grid = (query heads, query tiles in reverse order, sequences). Heads vary
 //     fastest and are ordered so that consecutive workgroups (which the hardware deals out to
@@ -14,21 +14,29 @@
 //     32x32 MFMAs, so the accumulator lands in the B-operand layout of O^T += V^T P^T: lane l
 //     holds query l%32. Key rows inside each 32-key block are loaded in a permuted order (bits 2
 //     and 3 of the row index swapped) so that accumulator slots t = 0..7 and 8..15 of lane l
-//     hold 8 CONSECUTIVE keys each: key = 32*kb + 16*(t>>3) + 8*(l>>5) + (t&7). Row max and row
-//     sum need one cross-lane exchange (lane l with lane l^32).
-//   * V^T comes from a pre-pass (vt_pack.hip) that stores every 64-key tile of V transposed and
-//     already swizzled, so the tile is one contiguous block and each P.V operand is a single
-//     16-byte LDS read.
-//   * K / K8 / k_scale / V^T tiles are double-buffered in LDS and filled with direct
-//     global->LDS loads issued one tile ahead; one barrier per tile separates the buffers.
-//     The fp16 Q of the workgroup stays in LDS (read only by FP16-routed tiles), the int8 Q of
-//     each wavefront in registers.
+//     hold 8 CONSECUTIVE keys each: key = 32*kb + 16*(t>>3) + 8*(l>>5) + (t&7).
 //   * the route bit of a key tile is uniform over each wavefront (route tiles are multiples of
 //     32 rows and 64 keys), so the FP16 / INT8 choice is a wave-uniform branch.
-//   * softmax in base 2 with the score scale folded into one FMA per element; the running max
-//     is only raised when a row's tile max exceeds it by more than 8 (so P < 256, exact in
-//     fp32 and fp16), which makes the O rescale rare; the row sum is taken from the
-//     fp16-rounded P that also feeds P.V.
+//
+// Software pipeline (per wavefront, in 32-key halves h of the 64-key tiles)
+//   Each step overlaps, in one straight-line block, the softmax of half h (VALU) with the P.V
+//   of half h-1 and the score MFMAs of half h+1 (matrix cores), so one wavefront keeps both
+//   pipes busy; the second wavefront of the SIMD fills what is left. One barrier per 64-key
+//   tile; K tiles (fp16 and/or int8, as the route bits of the workgroup ask) are fetched two
+//   tiles ahead and V^T tiles one tile ahead with direct global->LDS loads.
+//
+// Softmax
+//   Base 2, with the score scale folded into one FMA per element. The running max is only
+//   raised when needed: each half is exponentiated against the current max, and only if some
+//   lane's sum of P exceeds 2^15 (so that no P can overflow fp16) or the row has no max yet
+//   does the wavefront take the slow path, which takes the true max, rescales O and l and
+//   recomputes P. The row sum is taken from the fp16-rounded P that also feeds P.V and is kept
+//   per lane half until the epilogue.
+//
+// INT8 scores
+//   The int32 accumulator starts at the bit pattern of 1.5 * 2^23; as |q8 . k8| < 2^22 it then
+//   reads as the fp32 number 1.5 * 2^23 + q8 . k8 exactly, and one FMA with the per-key factors
+//   of the V^T pre-pass gives dk' * (q8 . k8) (see vt_pack.hip).
 #include "device_types.h"
 #include "launch.h"
 #include "tile_layout.h"
@@ -36,29 +44,35 @@
 namespace tilemix {
 namespace {
 
-constexpr int BN = kKeyTile;  // keys per inner-loop step
+constexpr int BN = kKeyTile;  // keys per pipeline tile
 constexpr int NW = 8;         // wavefronts per workgroup
 constexpr int ROWS_W = 32;    // query rows per wavefront
 constexpr int BM = NW * ROWS_W;
-constexpr float TAU = 8.0f;   // lazy-max threshold (log2 units)
+constexpr float P_LIMIT = 32768.0f;  // fast path: a lane's sum of P over a half stays below this
+constexpr int I8_BIAS = 0x4B400000;  // fp32 bits of 1.5 * 2^23
+// true: INT8 accumulators start at I8_BIAS and one FMA with (dk', bk) rescales them;
+// false: they start at 0 and are converted, then multiplied by dk'
+constexpr bool kBiasedI8 = false;
 
 // LDS layout. Rows are unpadded; 16-byte chunks are XOR-swizzled per row so that each 1 KiB
 // block stays contiguous (one direct wave load) while the rows one operand read touches fall in
 // distinct banks.
 template <int D>
 struct Smem {
-  static constexpr int RB16 = D * 2;   // bytes per fp16 row of K / Q
-  static constexpr int RB8 = D;        // bytes per int8 row of K8
+  static constexpr int RB16 = D * 2;  // bytes per fp16 row of K / Q
+  static constexpr int RB8 = D;       // bytes per int8 row of K8
   static constexpr int C16 = RB16 / 16;
   static constexpr int C8 = RB8 / 16;
-  static constexpr int Q16 = 0;                 // [BM][D] fp16 Q of the workgroup
-  static constexpr int STAGE0 = Q16 + BM * RB16;
-  static constexpr int K16 = 0;                 // offsets inside one stage
+  static constexpr int Q16 = 0;                   // [BM][D] fp16 Q of the workgroup
+  static constexpr int KBUF = Q16 + BM * RB16;    // two K stages
+  static constexpr int K16 = 0;                   // offsets inside one K stage
   static constexpr int K8 = K16 + BN * RB16;
-  static constexpr int DK = K8 + BN * RB8;
-  static constexpr int VT = DK + BN * 4;        // [D][BN] fp16 V^T, layout of vt_pack.hip
-  static constexpr int STAGE = VT + D * BN * 2;
-  static constexpr int BYTES = STAGE0 + 2 * STAGE;
+  static constexpr int KSTAGE = K8 + BN * RB8;
+  static constexpr int VBUF = KBUF + 2 * KSTAGE;  // two V^T stages, [D][BN] fp16 as vt_pack.hip
+  static constexpr int VSTAGE = D * BN * 2;
+  static constexpr int SBUF = VBUF + 2 * VSTAGE;  // three slots of per-key factors
+  static constexpr int SSLOT = 2 * BN * 4;        // dk'[BN], bk[BN]
+  static constexpr int BYTES = SBUF + 3 * SSLOT;
   // The 16 lanes served together read 16 different rows at one chunk index: XOR-ing the chunk
   // with (row / rows-per-256-bytes) puts them on 16 distinct 16-byte bank groups.
   __device__ static int f16(int r) { return (r / (256 / RB16)) & (C16 - 1); }
@@ -67,89 +81,350 @@ struct Smem {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-#define ONES2 half2v{static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)}
-
 __device__ __forceinline__ half2v pk(float a, float b) {
   return half2v{static_cast<_Float16>(a), static_cast<_Float16>(b)};  // v_cvt_pk_f16_f32 (RNE)
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// One direct global->LDS load per lane: `bytes` from src to lds_block + bytes * lane.
+// One direct global->LDS load per lane: 16 bytes from src to lds_block + 16 * lane.
 __device__ __forceinline__ void dma16(const void* src, char* lds_block) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_block, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void* src, char* lds_block) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_block, 4, 0, 0);
 }
 
 // Row index inside a 32-key block that MFMA row r reads: bits 2 and 3 swapped.
 __device__ __forceinline__ int perm32(int r) { return (r & 0x13) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-// Issue the direct loads of the key tile starting at j0 (sequence-local) into stage `buf`.
-// Rows past the sequence end read the last valid row; they are masked before use.
+// Direct global->LDS staging of the key-side tiles of one (sequence, KV head). Each wavefront
+// loads fixed 1 KiB blocks of every tile; the per-lane source offsets of those blocks are
+// computed once, so issuing a tile costs one address add per block.
 template <int D>
-__device__ __forceinline__ void stage_issue(const FwdArgs& a, char* buf, const _Float16* vt_tile,
-                                            int w, int lane, int j0, int Lk, int k_begin, int hk,
-                                            bool need16, bool need8, bool need_dk) {
+struct Stager {
   using L = Smem<D>;
-  auto key_of = [&](int row) { return static_cast<int64_t>(k_begin + min(j0 + row, Lk - 1)); };
-  constexpr int R16 = 1024 / L::RB16;  // K rows per wave load
-  constexpr int R8 = 1024 / L::RB8;
-  if (need16) {
-#pragma unroll
-    for (int blk = w; blk < BN / R16; blk += NW) {
-      const int row = blk * R16 + lane / L::C16;
-      const int chunk = (lane % L::C16) ^ L::f16(row);
-      dma16(a.k + key_of(row) * a.k_stride_tok + hk * a.k_stride_head + chunk * 8, buf + L::K16 + blk * 1024);
-    }
-  }
-  if (need8) {
-#pragma unroll
-    for (int blk = w; blk < BN / R8; blk += NW) {
-      const int row = blk * R8 + lane / L::C8;
-      const int chunk = (lane % L::C8) ^ L::f8(row);
-      dma16(a.k8 + (key_of(row) * a.hkv + hk) * D + chunk * 16, buf + L::K8 + blk * 1024);
-    }
-  }
-  if (need_dk && w == NW - 1)
-    dma4(a.k_scale + static_cast<int64_t>(hk) * a.total_k + key_of(lane), buf + L::DK);
-  const char* vsrc = reinterpret_cast<const char*>(vt_tile);
-#pragma unroll
-  for (int blk = w; blk < D * BN * 2 / 1024; blk += NW) dma16(vsrc + blk * 1024 + lane * 16, buf + L::VT + blk * 1024);
-}
+  static constexpr int R16 = 1024 / L::RB16;  // K rows per 1 KiB block
+  static constexpr int R8 = 1024 / L::RB8;
+  static constexpr int NB16 = BN / R16;       // blocks per K tile
+  static constexpr int NB8 = BN / R8;
+  static constexpr int NBV = D * BN * 2 / 1024;
+  static constexpr int I16 = (NB16 + NW - 1) / NW;  // blocks per wave
+  static constexpr int I8 = (NB8 + NW - 1) / NW;
+  static constexpr int IV = (NBV + NW - 1) / NW;
 
-// Route bits of the workgroup's wavefronts for the key tile starting at j0: bit w = route bit of
-// wave w, bit 16+w = wave w computes the tile at all (it has rows in the sequence and not all of
-// them are causally masked).
-__device__ __forceinline__ uint32_t tile_bits(const FwdArgs& a, const uint64_t* words_hk, int mt0,
-                                              int q0, int Lq, int off, int j0) {
-  const int gj = (j0 / a.bn_r) / a.group;
-  uint32_t bits = 0;
+  // Uniform byte pointers (scalar registers); the small per-lane byte offsets are recomputed at
+  // every issue from an opaque copy of the lane id (a few VALU operations) rather than kept live.
+  const char* k16;   // key 0 of the sequence, this KV head, fp16 K
+  const char* k8;    // the same, int8 K
+  const char* vt;    // V^T tile 0
+  const char* ks;    // factors of tile 0
+  int64_t st16;      // bytes between consecutive keys, fp16 K
+  int64_t st8;       // bytes between consecutive keys, int8 K
+  int w, Lk;
+
+  __device__ void init(const FwdArgs& a, int k_begin, int hk, int Lk_, int w_, int64_t tile0) {
+    w = w_;
+    Lk = Lk_;
+    st16 = a.k_stride_tok * 2;
+    st8 = static_cast<int64_t>(a.hkv) * D;
+    k16 = reinterpret_cast<const char*>(a.k) + k_begin * st16 + hk * a.k_stride_head * 2;
+    k8 = reinterpret_cast<const char*>(a.k8) + static_cast<int64_t>(k_begin) * st8 + static_cast<int64_t>(hk) * D;
+    vt = reinterpret_cast<const char*>(a.vt + tile0 * (D * BN));
+    ks = reinterpret_cast<const char*>(a.ks + tile0 * (2 * BN));
+  }
+  __device__ static int opaque_lane() {
+    int l = threadIdx.x & 63;
+    asm volatile("" : "+v"(l));
+    return l;
+  }
+
+  // K tile n into stage buf: fp16 rows if need16, int8 rows if need8. Rows past the sequence
+  // end repeat the last key; the kernel masks them before use.
+  __device__ __forceinline__ void k_tile(char* buf, int n, bool need16, bool need8) const {
+    const int j0 = n * BN;
+    const int last = Lk - 1 - j0;  // rows beyond it repeat it
+    const int lane = opaque_lane();
+    if (need16) {
+      const char* base = k16 + static_cast<int64_t>(j0) * st16;
 #pragma unroll
-  for (int wv = 0; wv < NW; ++wv) {
-    const int qa = q0 + ROWS_W * wv;
-    const int qlast = min(qa + ROWS_W - 1, Lq - 1);
-    const bool act = qa < Lq && !(a.causal && j0 > qlast + off);
-    if (act) {
-      const uint64_t word = words_hk[static_cast<int64_t>(mt0 + qa / a.bm_r) * a.wpr + (gj >> 6)];
-      bits |= (static_cast<uint32_t>((word >> (gj & 63)) & 1u) << wv) | (1u << (16 + wv));
+      for (int i = 0; i < I16; ++i) {
+        if (w + NW * i >= NB16) break;
+        const int row = (w + NW * i) * R16 + lane / L::C16;
+        const uint32_t chunk = ((lane % L::C16) ^ L::f16(row)) * 16;
+        dma16(base + (static_cast<uint32_t>(min(row, last) * st16) + chunk), buf + L::K16 + (w + NW * i) * 1024);
+      }
+    }
+    if (need8) {
+      const char* base = k8 + static_cast<int64_t>(j0) * st8;
+#pragma unroll
+      for (int i = 0; i < I8; ++i) {
+        if (w + NW * i >= NB8) break;
+        const int row = (w + NW * i) * R8 + lane / L::C8;
+        const uint32_t chunk = ((lane % L::C8) ^ L::f8(row)) * 16;
+        dma16(base + (static_cast<uint32_t>(min(row, last) * st8) + chunk), buf + L::K8 + (w + NW * i) * 1024);
+      }
     }
   }
+
+  // Pre-transposed V^T tile n (contiguous in the workspace) into stage buf.
+  __device__ __forceinline__ void v_tile(char* buf, int n) const {
+    const char* src = vt + static_cast<int64_t>(n) * (D * BN * 2);
+    const uint32_t lo = static_cast<uint32_t>(opaque_lane() * 16);
+#pragma unroll
+    for (int i = 0; i < IV; ++i) {
+      if (w + NW * i >= NBV) break;
+      dma16(src + (w + NW * i) * 1024 + lo, buf + (w + NW * i) * 1024);
+    }
+  }
+
+  // The 512 bytes of per-key factors of tile n into a factor slot.
+  __device__ __forceinline__ void scales(char* buf, int n) const {
+    const int lane = opaque_lane();
+    if (w == NW - 1 && lane < 32)
+      dma16(ks + static_cast<int64_t>(n) * (2 * BN * 4) + static_cast<uint32_t>(lane * 16), buf);
+  }
+};
+
+typedef const __attribute__((address_space(4))) uint64_t const_u64;
+typedef const __attribute__((address_space(4))) int32_t const_i32;
+
+// Workgroup-uniform metadata (sequence offsets, route words) is read through the constant
+// address space, so that it lands in scalar registers via scalar loads; the kernel never writes it.
+__device__ __forceinline__ int ld_uniform(const int32_t* p, int i) { return ((const const_i32*)p)[i]; }
+
+// Route bits of the workgroup's route rows for key-tile group gj: bit r = route row rr0 + r.
+// The words are read through the constant address space (scalar loads).
+__device__ __forceinline__ uint32_t group_bits(const const_u64* wrow, int wpr, int nrr, int gj) {
+  uint32_t bits = 0;
+  const int wi = gj >> 6, sh = gj & 63;
+  for (int r = 0; r < nrr; ++r)
+    bits |= static_cast<uint32_t>((wrow[static_cast<int64_t>(r) * wpr + wi] >> sh) & 1u) << r;
   return bits;
 }
 
-__device__ __forceinline__ bool any_fp16(uint32_t bits) { return ((bits >> 16) & ~bits & 0xffu) != 0; }
-__device__ __forceinline__ bool any_int8(uint32_t bits) { return ((bits >> 16) & bits & 0xffu) != 0; }
-
+// Per-wavefront registers: constants of the wave's rows and the online-softmax state.
+// Per-wavefront registers: constants of the wave's rows and the online-softmax state.
 template <int D, bool KV8>
+struct Wave {
+  int hl, my_q;
+  int lim;         // last legal key (sequence-local) of this lane's query
+  bool row_valid;
+  // LDS byte offsets of this lane's operand rows: chunk (2*i + hl) ^ f of a row whose length is a
+  // multiple of 128 bytes sits at row_start + 16*(hl ^ f) XOR 32*i, since 2*i + hl = 2*i ^ hl
+  int kbase8, vbase;      // K8 row (i = ks), V^T row (i = 16-key step)
+  int kbase16, qbase16;   // fp16 K and Q rows (i = ks)
+  int4v q8f[D / 32];
+  int16v bias;     // starting value of the INT8 accumulators (I8_BIAS or 0)
+  float cq;        // q_scale * softmax_scale * log2(e), floored so that 0 * -inf cannot occur
+  float cs;        // softmax_scale * log2(e)
+  float16v o[D / 32];  // O^T accumulator
+  float16v s[2];       // fp32 scores of the two key halves, in units of 1 / c[half]
+  float c[2];          // per-row factor of each half to log2 units: cq (INT8) or cs (FP16)
+  half8v p[2][2];      // fp16 P of the two key halves, [half][16-key step]
+  float m, m_use, l;   // running max (log2 units), its finite stand-in, this lane's row sum
+
+  // s[KB] = scores of key half KB of the K tile in stage kst; scl = that tile's per-key factors.
+  // With DUMP, the raw int32 accumulators of an INT8 half also go to the debug dump when
+  // dump_row is not NULL: key j of this lane's query row is dump_row[(j / bn_r) * tile_stride +
+  // j % bn_r], for the keys j < Lk; key0 = sequence-local index of the half's first key.
+  template <int KB, bool I8, bool DUMP>
+  __device__ __forceinline__ void qk(const char* kst, const char* q16, const float* scl, int32_t* dump_row,
+                                     int key0, int Lk, int bn_r, int tile_stride) {
+    using L = Smem<D>;
+    if constexpr (I8) {
+      int16v acc = kBiasedI8 ? bias : int16v{};
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) {
+        const int4v kf = *reinterpret_cast<const int4v*>(kst + L::K8 + KB * 32 * L::RB8 + (kbase8 ^ (32 * ks)));
+        acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, q8f[ks], acc, 0, 0, 0);
+      }
+      if constexpr (DUMP) {
+        if (dump_row != nullptr) {
+#pragma unroll
+          for (int t = 0; t < 16; ++t) {
+            const int key = key0 + 16 * (t >> 3) + 8 * hl + (t & 7);
+            if (key < Lk) dump_row[(key / bn_r) * tile_stride + key % bn_r] = acc[t] - (kBiasedI8 ? I8_BIAS : 0);
+          }
+        }
+      }
+#pragma unroll
+      for (int g8 = 0; g8 < 2; ++g8) {
+        const int kidx = 32 * KB + 16 * g8 + 8 * hl;
+        const float4v d0 = *reinterpret_cast<const float4v*>(scl + kidx);
+        const float4v d1 = *reinterpret_cast<const float4v*>(scl + kidx + 4);
+        float4v b0 = {}, b1 = {};
+        if constexpr (kBiasedI8) {
+          b0 = *reinterpret_cast<const float4v*>(scl + BN + kidx);
+          b1 = *reinterpret_cast<const float4v*>(scl + BN + kidx + 4);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float dk = e < 4 ? d0[e] : d1[e - 4];
+          if constexpr (kBiasedI8)
+            s[KB][8 * g8 + e] = __builtin_fmaf(__builtin_bit_cast(float, acc[8 * g8 + e]), dk, e < 4 ? b0[e] : b1[e - 4]);
+          else
+            s[KB][8 * g8 + e] = static_cast<float>(acc[8 * g8 + e]) * dk;
+        }
+      }
+      c[KB] = cq;
+    } else {
+      float16v acc = {};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const half8v qv = *reinterpret_cast<const half8v*>(q16 + (qbase16 ^ (32 * ks)));
+        const half8v kf = *reinterpret_cast<const half8v*>(kst + L::K16 + KB * 32 * L::RB16 + (kbase16 ^ (32 * ks)));
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qv, acc, 0, 0, 0);
+      }
+      if constexpr (KV8) {
+        // K of the INT8 cache enters the FP16 path as exact fp16(k8): apply its scale here
+#pragma unroll
+        for (int g8 = 0; g8 < 2; ++g8) {
+          const int kidx = 32 * KB + 16 * g8 + 8 * hl;
+          const float4v d0 = *reinterpret_cast<const float4v*>(scl + kidx);
+          const float4v d1 = *reinterpret_cast<const float4v*>(scl + kidx + 4);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s[KB][8 * g8 + e] = acc[8 * g8 + e] * (e < 4 ? d0[e] : d1[e - 4]);
+        }
+      } else {
+        s[KB] = acc;
+      }
+      c[KB] = cs;
+    }
+  }
+
+  // Legality mask of half KB (causal diagonal, sequence tail): illegal scores become -inf.
+  template <int KB>
+  __device__ __forceinline__ void mask(int key0) {
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+      if (key0 + 16 * (t >> 3) + 8 * hl + (t & 7) > lim) s[KB][t] = -INFINITY;
+  }
+
+  // p[KB] = fp16 exp2(s * c - m_use) of half KB; returns this lane's sum of the rounded P.
+  template <int KB>
+  __device__ __forceinline__ float softmax() {
+    float rs = 0.0f;
+    const float ck = c[KB];
+#pragma unroll
+    for (int g8 = 0; g8 < 2; ++g8) {
+      half8v pb;
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float x0 = __builtin_fmaf(s[KB][8 * g8 + e], ck, -m_use);
+        const float x1 = __builtin_fmaf(s[KB][8 * g8 + e + 1], ck, -m_use);
+        const half2v h2 = pk(fast_exp2(x0), fast_exp2(x1));
+        pb[e] = h2[0];
+        pb[e + 1] = h2[1];
+        rs = __builtin_amdgcn_fdot2(h2, half2v{static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)}, rs, false);
+      }
+      p[KB][g8] = pb;
+    }
+    return rs;
+  }
+
+  // This lane's sum of the fp16 P of half KB, in the order softmax() adds it.
+  template <int KB>
+  __device__ __forceinline__ float psum() const {
+    float r = 0.0f;
+#pragma unroll
+    for (int g8 = 0; g8 < 2; ++g8)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2)
+        r = __builtin_amdgcn_fdot2(half2v{p[KB][g8][e], p[KB][g8][e + 1]},
+                                   half2v{static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)}, r, false);
+    return r;
+  }
+
+  // Slow path of half KB: raise the running max to the half's true max, rescale O and l (and the
+  // fp16 P of half PENDING, if >= 0, whose P.V is still to come), and recompute P. Wave-uniform.
+  template <int KB, int PENDING>
+  __device__ __forceinline__ float rescale() {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) mx = fmaxf(mx, s[KB][t] * c[KB]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (mx > m) {  // false while both are -inf
+      const float alpha = fast_exp2(m - mx);  // m = -inf: alpha = 0 (O and l are still 0)
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) o[i] *= alpha;
+      if constexpr (PENDING >= 0) {
+        // the pending P is rescaled in fp32 and re-rounded; its share of l is rebuilt from the
+        // re-rounded values, so that O and l keep receiving identical weights
+        const float old_sum = psum<PENDING>();
+#pragma unroll
+        for (int g8 = 0; g8 < 2; ++g8)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            p[PENDING][g8][e] = static_cast<_Float16>(static_cast<float>(p[PENDING][g8][e]) * alpha);
+        l = (l - old_sum) * alpha + psum<PENDING>();
+      } else {
+        l *= alpha;
+      }
+      m = mx;
+      m_use = mx;
+    }
+    return softmax<KB>();
+  }
+
+  // Finish half KB after its softmax: take the slow path if needed, then add the row sum.
+  template <int KB, int PENDING = -1>
+  __device__ __forceinline__ void settle(float rs) {
+    if (__any(row_valid && (!(rs <= P_LIMIT) || m == -INFINITY))) rs = rescale<KB, PENDING>();
+    l += rs;
+  }
+
+  // O^T += V^T P^T for key half KB of the V^T tile in stage vst.
+  template <int KB>
+  __device__ __forceinline__ void pv(const char* vst) {
+#pragma unroll
+    for (int g8 = 0; g8 < 2; ++g8) {
+      const int kk = 2 * KB + g8;
+#pragma unroll
+      for (int dblk = 0; dblk < D / 32; ++dblk) {
+        const half8v vf = *reinterpret_cast<const half8v*>(vst + dblk * 32 * (BN * 2) + (vbase ^ (32 * kk)));
+        o[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, p[KB][g8], o[dblk], 0, 0, 0);
+      }
+    }
+  }
+};
+
+// Where the debug dump of the current tiles goes (DUMP instances only).
+struct DumpCtx {
+  int32_t* row;  // this lane's query row in the dump (NULL: not dumped); see Wave::qk
+  int bn_r, tile_stride, Lk;
+  int act_limit;  // a key tile starting at j0 is dumped iff j0 <= act_limit
+};
+
+// Scores of half KB of the tile at key j0 with the route chosen by I8 (and the dump, if any).
+template <int KB, bool I8, bool DUMP, int D, bool KV8>
+__device__ __forceinline__ void qk_tile(Wave<D, KV8>& wv, const char* kst, const char* q16, const float* scl,
+                                        int j0, const DumpCtx& dc) {
+  int32_t* row = (DUMP && I8 && j0 <= dc.act_limit) ? dc.row : nullptr;
+  wv.template qk<KB, I8, DUMP>(kst, q16, scl, row, j0 + 32 * KB, dc.Lk, dc.bn_r, dc.tile_stride);
+}
+
+// One main-loop iteration of a run whose tiles n and n+1 share this wave's route I8 and need no
+// mask: the softmax of a key half overlaps the P.V of the previous half and the score MFMAs of
+// the next one, in straight-line code apart from the rare slow path.
+template <int D, bool KV8, bool I8>
+__device__ __forceinline__ void run_iter(Wave<D, KV8>& wv, const char* vst, const char* kst, const char* q16,
+                                         const float* scl_n1) {
+  float rs = wv.template softmax<1>();
+  wv.template pv<0>(vst);
+  wv.template qk<0, I8, false>(kst, q16, scl_n1, nullptr, 0, 0, 1, 0);
+  wv.template settle<1>(rs);
+  rs = wv.template softmax<0>();
+  wv.template pv<1>(vst);
+  wv.template qk<1, I8, false>(kst, q16, scl_n1, nullptr, 0, 0, 1, 0);
+  wv.template settle<0>(rs);
+}
+
+template <int D, bool KV8, bool DUMP>
 __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a) {
   using L = Smem<D>;
   __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (scalar)
   const int hl = lane >> 5;   // half of the wave: selects 8 of the 16 keys of a k-step
   const int r32 = lane & 31;  // query row of this lane within the wave
 
@@ -160,10 +435,10 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
   const int b = blockIdx.z;
   const int n_ct = (a.max_seqlen_q + BM - 1) / BM;
   const int c = n_ct - 1 - static_cast<int>(blockIdx.y);
-  const int q_begin = a.cu_q[b];
-  const int Lq = a.cu_q[b + 1] - q_begin;
-  const int k_begin = a.cu_k[b];
-  const int Lk = a.cu_k[b + 1] - k_begin;
+  const int q_begin = ld_uniform(a.cu_q, b);
+  const int Lq = ld_uniform(a.cu_q, b + 1) - q_begin;
+  const int k_begin = ld_uniform(a.cu_k, b);
+  const int Lk = ld_uniform(a.cu_k, b + 1) - k_begin;
   const int q0 = c * BM;
   if (q0 >= Lq) return;  // uniform over the workgroup
 
@@ -174,28 +449,44 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
   const int n_tiles = key_end > 0 ? (key_end + BN - 1) / BN : 0;
 
   const int qa = q0 + ROWS_W * w;  // first query row of this wave
-  const int my_q = qa + r32;
-  const bool row_valid = my_q < Lq;
-  const uint64_t* words_hk = a.words + static_cast<int64_t>(hk) * a.total_mtiles * a.wpr;
-  const int mt0 = a.cu_mtiles[b];
-  char* const stage0 = smem + L::STAGE0;
-  const _Float16* vt_head =
-      a.vt + (static_cast<int64_t>(hk) * a.vt_tiles + key_tiles_before(a.cu_k, b)) * (D * BN);
+  const bool wave_live = qa < Lq;
+  const int qlast_w = min(qa + ROWS_W - 1, Lq - 1);
+  // tiles [0, n_full) need no legality mask for any row of this wave
+  const int n_full = (a.causal ? min(Lk, qa + off + 1) : Lk) / BN;
 
-  // ---- per-lane LDS offsets of the MFMA operands (kb / dblk / kk steps are immediates)
-  const int kr = perm32(r32);  // K row this lane feeds to the MFMA
-  int koff16[D / 16], qoff16[D / 16];
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    koff16[ks] = kr * L::RB16 + 16 * ((2 * ks + hl) ^ L::f16(kr));
-    qoff16[ks] = (ROWS_W * w + r32) * L::RB16 + 16 * ((2 * ks + hl) ^ L::f16(ROWS_W * w + r32));
+  // route rows of the workgroup and the wave's own one
+  const int mt0 = ld_uniform(a.cu_mtiles, b);
+  const int rr0 = q0 / a.bm_r;
+  const int nrr = q_last / a.bm_r - rr0 + 1;
+  const int my_rl = wave_live ? qa / a.bm_r - rr0 : 0;
+  const uint32_t full = (1u << nrr) - 1u;
+  const const_u64* wrow = (const const_u64*)(a.words) +  // scalar loads; the words are read-only here
+                          (static_cast<int64_t>(hk) * a.total_mtiles + mt0 + rr0) * a.wpr;
+  const int tpg = (a.bn_r / BN) * a.group;  // pipeline tiles per routing bit
+
+  Stager<D> stg;
+  int tiles_before = 0;  // 64-key tiles of the sequences before b (tiles never straddle sequences)
+  for (int i = 0; i < b; ++i) tiles_before += (ld_uniform(a.cu_k, i + 1) - ld_uniform(a.cu_k, i) + BN - 1) / BN;
+  stg.init(a, k_begin, hk, Lk, w, static_cast<int64_t>(hk) * a.vt_tiles + tiles_before);
+  char* const kbuf = smem + L::KBUF;
+  char* const vbuf = smem + L::VBUF;
+  char* const sbuf = smem + L::SBUF;
+  const char* const q16w = smem + L::Q16;
+
+  Wave<D, KV8> wv;
+  wv.hl = hl;
+  wv.my_q = qa + r32;
+  wv.lim = a.causal ? min(Lk - 1, wv.my_q + off) : Lk - 1;
+  wv.row_valid = wv.my_q < Lq;
+  {
+    const int kr = perm32(r32);  // K row this lane feeds to the MFMA
+    wv.kbase16 = kr * L::RB16 + 16 * (hl ^ L::f16(kr));
+    wv.qbase16 = (ROWS_W * w + r32) * L::RB16 + 16 * (hl ^ L::f16(ROWS_W * w + r32));
+    wv.kbase8 = kr * L::RB8 + 16 * (hl ^ L::f8(kr));
+    wv.vbase = r32 * (BN * 2) + 16 * (hl ^ vt_swizzle(r32));
   }
-  int koff8[D / 32];
 #pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks) koff8[ks] = kr * L::RB8 + 16 * ((2 * ks + hl) ^ L::f8(kr));
-  int voff[BN / 16];  // V^T row r32 (+32*dblk), chunk 2*kk + hl
-#pragma unroll
-  for (int kk = 0; kk < BN / 16; ++kk) voff[kk] = r32 * (BN * 2) + 16 * ((2 * kk + hl) ^ vt_swizzle(r32));
+  for (int i = 0; i < 16; ++i) wv.bias[i] = kBiasedI8 ? I8_BIAS : 0;
 
   // ---- resident queries: fp16 Q of the workgroup in LDS, this wave's int8 Q in registers
   for (int ch = tid; ch < BM * L::C16; ch += NW * 64) {
@@ -206,175 +497,159 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
                                             static_cast<int64_t>(h) * a.q_stride_head + col * 8);
     *reinterpret_cast<int4v*>(smem + L::Q16 + row * L::RB16 + 16 * (col ^ L::f16(row))) = val;
   }
-  int4v q8f[D / 32];
-  float cq = 1e-30f;  // q_scale * softmax_scale * log2(e), floored so that 0 * -inf cannot occur
-  if (row_valid) {
-    const int64_t tq = q_begin + my_q;
+  wv.cq = 1e-30f;
+  wv.cs = a.scale_log2;
+  if (wv.row_valid) {
+    const int64_t tq = q_begin + wv.my_q;
     const int8_t* q8p = a.q8 + (tq * a.hq + h) * D;
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) q8f[ks] = *reinterpret_cast<const int4v*>(q8p + 32 * ks + 16 * hl);
-    cq = fmaxf(a.q_scale[static_cast<int64_t>(h) * a.total_q + tq] * a.scale_log2, 1e-30f);
+    for (int ks = 0; ks < D / 32; ++ks) wv.q8f[ks] = *reinterpret_cast<const int4v*>(q8p + 32 * ks + 16 * hl);
+    wv.cq = fmaxf(a.q_scale[static_cast<int64_t>(h) * a.total_q + tq] * a.scale_log2, 1e-30f);
   } else {
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) q8f[ks] = int4v{};
+    for (int ks = 0; ks < D / 32; ++ks) wv.q8f[ks] = int4v{};
+  }
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) wv.o[i] = float16v{};
+  wv.m = -INFINITY;
+  wv.m_use = 0.0f;
+  wv.l = 0.0f;
+
+  DumpCtx dc{};
+  if (DUMP) {
+    const int my_rr = mt0 + qa / a.bm_r;
+    const bool dump_me = h == a.dump_head && wave_live && wv.row_valid && my_rr >= a.dump_m0 &&
+                         my_rr < a.dump_m0 + a.dump_mcount;
+    dc.row = dump_me ? a.dump + (static_cast<int64_t>(my_rr - a.dump_m0) * a.dump_ntiles * a.bm_r +
+                                 wv.my_q % a.bm_r) * a.bn_r
+                     : nullptr;
+    dc.bn_r = a.bn_r;
+    dc.tile_stride = a.bm_r * a.bn_r;
+    dc.Lk = Lk;
+    dc.act_limit = a.causal ? qlast_w + off : 0x7fffffff;
   }
 
-  float16v o[D / 32];
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i) o[i] = float16v{};
-  float m_i = -INFINITY;  // running max, log2 domain
-  float l_i = 0.0f;       // running normaliser
+  // route bits of the workgroup's rows for tiles n, n+1, n+2 (bit r = route row rr0 + r)
+  uint32_t rb0 = 0, rb1 = 0, rb2 = 0, rb3 = 0;
+  if (n_tiles > 0) rb0 = group_bits(wrow, a.wpr, nrr, 0);
+  if (n_tiles > 1) rb1 = (1 % tpg) ? rb0 : group_bits(wrow, a.wpr, nrr, 1 / tpg);
+  if (n_tiles > 2) rb2 = (2 % tpg) ? rb1 : group_bits(wrow, a.wpr, nrr, 2 / tpg);
 
-  const int my_rr = mt0 + qa / a.bm_r;
-  const bool dump_me = a.dump != nullptr && h == a.dump_head && qa < Lq && my_rr >= a.dump_m0 &&
-                       my_rr < a.dump_m0 + a.dump_mcount;
-
-  // ---- prologue: tile 0 into stage 0
-  uint32_t bits_next = n_tiles > 0 ? tile_bits(a, words_hk, mt0, q0, Lq, off, 0) : 0;
-  if (n_tiles > 0)
-    stage_issue<D>(a, stage0, vt_head, w, lane, 0, Lk, k_begin, hk, any_fp16(bits_next),
-                   any_int8(bits_next), any_int8(bits_next) || KV8);
+  // ---- prologue: K tiles 0 and 1, V^T tile 0, factors of tiles 0 and 1
+  if (n_tiles > 0) {
+    stg.k_tile(kbuf, 0, rb0 != full, rb0 != 0u);
+    stg.v_tile(vbuf, 0);
+    stg.scales(sbuf, 0);
+  }
+  if (n_tiles > 1) {
+    stg.k_tile(kbuf + L::KSTAGE, 1, rb1 != full, rb1 != 0u);
+    stg.scales(sbuf + L::SSLOT, 1);
+  }
   __syncthreads();
 
-  for (int n = 0; n < n_tiles; ++n) {
-    const int j0 = n * BN;
-    const uint32_t bits = bits_next;
-    const char* cur = stage0 + (n & 1) * L::STAGE;
-    if (n + 1 < n_tiles) {
-      bits_next = tile_bits(a, words_hk, mt0, q0, Lq, off, j0 + BN);
-      stage_issue<D>(a, stage0 + ((n + 1) & 1) * L::STAGE, vt_head + (n + 1) * (D * BN), w, lane,
-                     j0 + BN, Lk, k_begin, hk, any_fp16(bits_next), any_int8(bits_next),
-                     any_int8(bits_next) || KV8);
+  if (wave_live && n_tiles > 0) {
+    const float* scl0 = reinterpret_cast<const float*>(sbuf);
+    if ((rb0 >> my_rl) & 1u) {
+      qk_tile<0, true, DUMP>(wv, kbuf, q16w, scl0, 0, dc);
+      qk_tile<1, true, DUMP>(wv, kbuf, q16w, scl0, 0, dc);
+    } else {
+      qk_tile<0, false, DUMP>(wv, kbuf, q16w, scl0, 0, dc);
+      qk_tile<1, false, DUMP>(wv, kbuf, q16w, scl0, 0, dc);
     }
+    if (n_full < 1) wv.template mask<0>(0);
+    wv.template settle<0>(wv.template softmax<0>());
+  }
 
-    if ((bits >> (16 + w)) & 1u) {
-      const float* dk = reinterpret_cast<const float*>(cur + L::DK);
-      float16v s[2];  // [key block], pre-softmax units
-      float cs;
-      if ((bits >> w) & 1u) {
-        // ---- INT8 path: int32 accumulation, then per-key scale (per-query scale folded in cs)
-        int16v acc[2] = {};
-#pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) {
-          const int4v k0 = *reinterpret_cast<const int4v*>(cur + L::K8 + koff8[ks]);
-          const int4v k1 = *reinterpret_cast<const int4v*>(cur + L::K8 + 32 * L::RB8 + koff8[ks]);
-          acc[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(k0, q8f[ks], acc[0], 0, 0, 0);
-          acc[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1, q8f[ks], acc[1], 0, 0, 0);
-        }
-        if (dump_me && row_valid) {
-          const int64_t rbase = static_cast<int64_t>(my_rr - a.dump_m0) * a.dump_ntiles;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-              const int key = j0 + 32 * kb + 16 * (t >> 3) + 8 * hl + (t & 7);
-              if (key < Lk)
-                a.dump[((rbase + key / a.bn_r) * a.bm_r + my_q % a.bm_r) * a.bn_r + key % a.bn_r] = acc[kb][t];
-            }
-        }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int g8 = 0; g8 < 2; ++g8) {
-            const float4v d0 = *reinterpret_cast<const float4v*>(dk + 32 * kb + 16 * g8 + 8 * hl);
-            const float4v d1 = *reinterpret_cast<const float4v*>(dk + 32 * kb + 16 * g8 + 8 * hl + 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              s[kb][8 * g8 + e] = static_cast<float>(acc[kb][8 * g8 + e]) * d0[e];
-              s[kb][8 * g8 + 4 + e] = static_cast<float>(acc[kb][8 * g8 + 4 + e]) * d1[e];
-            }
-          }
-        cs = cq;
-      } else {
-        // ---- FP16 path
-        float16v acc[2] = {};
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const half8v qv = *reinterpret_cast<const half8v*>(smem + L::Q16 + qoff16[ks]);
-          const half8v k0 = *reinterpret_cast<const half8v*>(cur + L::K16 + koff16[ks]);
-          const half8v k1 = *reinterpret_cast<const half8v*>(cur + L::K16 + 32 * L::RB16 + koff16[ks]);
-          acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0, qv, acc[0], 0, 0, 0);
-          acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1, qv, acc[1], 0, 0, 0);
-        }
-        if (KV8) {
-          // K of the INT8 cache enters the FP16 path as exact fp16(k8): apply its scale here
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int g8 = 0; g8 < 2; ++g8) {
-              const float4v d0 = *reinterpret_cast<const float4v*>(dk + 32 * kb + 16 * g8 + 8 * hl);
-              const float4v d1 = *reinterpret_cast<const float4v*>(dk + 32 * kb + 16 * g8 + 8 * hl + 4);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                s[kb][8 * g8 + e] = acc[kb][8 * g8 + e] * d0[e];
-                s[kb][8 * g8 + 4 + e] = acc[kb][8 * g8 + 4 + e] * d1[e];
-              }
-            }
-        } else {
-          s[0] = acc[0];
-          s[1] = acc[1];
-        }
-        cs = a.scale_log2;  // fp16 Q is not quantized: only the softmax scale remains
-      }
+  // ---- main loop: iteration n finishes tile n and starts tile n+1. Runs of iterations whose
+  // two tiles are INT8-routed for this wave and need no mask go through a branch-free specialised
+  // loop; the rest (FP16 tiles, route changes, diagonal and tail tiles, the last tile, the debug
+  // dump) through a generic iteration.
+  int g3 = 2 / tpg, tig3 = 2 % tpg;  // group of tile n+2 and its index within the group
+  int slot_n = 0;                    // factor slot of tile n (tiles rotate through three slots)
+  const bool fast_ok = wave_live && !DUMP;
 
-      // ---- legality mask (diagonal and tail tiles only)
-      if ((j0 + BN > Lk) || (a.causal && j0 + BN - 1 > qa + off)) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int t = 0; t < 16; ++t) {
-            const int key = j0 + 32 * kb + 16 * (t >> 3) + 8 * hl + (t & 7);
-            const bool legal = key < Lk && (!a.causal || key <= my_q + off);
-            if (!legal) s[kb][t] = -INFINITY;
-          }
-      }
-
-      // ---- online softmax (Section 3.1 recurrence), base 2, lazy max
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int t = 0; t < 16; t += 2) mx = fmaxf(fmaxf(mx, s[kb][t]), s[kb][t + 1]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float tile_max = mx * cs;  // cs > 0
-      if (__any(tile_max > m_i + TAU)) {
-        const float m_new = tile_max > m_i + TAU ? tile_max : m_i;
-        const float alpha = m_new > m_i ? fast_exp2(m_i - m_new) : 1.0f;
-        l_i *= alpha;
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i) o[i] *= alpha;
-        m_i = m_new;
-      }
-      const float m_use = m_i == -INFINITY ? 0.0f : m_i;
-
-      // ---- P = exp2(s*c - m) in fp16, O^T += V^T P^T (16 keys per MFMA step)
-      float rs = 0.0f;
-#pragma unroll
-      for (int kk = 0; kk < BN / 16; ++kk) {
-        half8v pb;
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const half2v h2 = pk(fast_exp2(fmaf(s[kk >> 1][8 * (kk & 1) + e], cs, -m_use)),
-                               fast_exp2(fmaf(s[kk >> 1][8 * (kk & 1) + e + 1], cs, -m_use)));
-          pb[e] = h2[0];
-          pb[e + 1] = h2[1];
-          rs = __builtin_amdgcn_fdot2(h2, ONES2, rs, false);
-        }
-#pragma unroll
-        for (int dblk = 0; dblk < D / 32; ++dblk) {
-          const half8v vf = *reinterpret_cast<const half8v*>(cur + L::VT + dblk * 32 * (BN * 2) + voff[kk]);
-          o[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pb, o[dblk], 0, 0, 0);
-        }
-      }
-      l_i += rs + __shfl_xor(rs, 32);
+  // barrier, then the direct loads of K_{n+2}, its factors and V_{n+1}; route bits of tile n+3
+  auto begin_iter = [&](int n) {
+    __syncthreads();  // K_{n+1}, V_n and their factors landed; stages of K_n and V_{n-1} free
+    if (n + 2 < n_tiles) {
+      stg.k_tile(kbuf + (n & 1) * L::KSTAGE, n + 2, rb2 != full, rb2 != 0u);
+      stg.scales(sbuf + (slot_n == 0 ? 2 : slot_n - 1) * L::SSLOT, n + 2);
     }
-    __syncthreads();  // waits for this thread's direct loads, then for everyone's
+    if (n + 1 < n_tiles) stg.v_tile(vbuf + ((n + 1) & 1) * L::VSTAGE, n + 1);
+    rb3 = rb2;
+    if (++tig3 == tpg) {
+      tig3 = 0;
+      ++g3;
+      if (n + 3 < n_tiles) rb3 = group_bits(wrow, a.wpr, nrr, g3);
+    }
+  };
+  auto end_iter = [&]() {
+    rb0 = rb1;
+    rb1 = rb2;
+    rb2 = rb3;
+    slot_n = slot_n == 2 ? 0 : slot_n + 1;
+  };
+  // iteration n can take the specialised loop: tiles n and n+1 exist, are both INT8-routed for
+  // this wave and need no mask (FP16 runs take the generic iteration, which keeps the register
+  // footprint of the kernel within two waves per SIMD without spills)
+  auto fast = [&](int n) {
+    return fast_ok && n + 1 < n_tiles && n + 1 < n_full && (((rb0 & rb1) >> my_rl) & 1u) != 0u;
+  };
+  auto scl_of = [&](int slot) { return reinterpret_cast<const float*>(sbuf + slot * L::SSLOT); };
+  auto slot_next = [&]() { return slot_n == 2 ? 0 : slot_n + 1; };
+
+  for (int n = 0; n < n_tiles;) {
+    if (fast(n)) {
+      do {
+        begin_iter(n);
+        run_iter<D, KV8, true>(wv, vbuf + (n & 1) * L::VSTAGE, kbuf + ((n + 1) & 1) * L::KSTAGE, q16w,
+                               scl_of(slot_next()));
+        end_iter();
+        ++n;
+      } while (fast(n));
+      continue;
+    }
+    begin_iter(n);
+    if (wave_live) {
+      // the two pipeline steps in sequence, with the route and mask chosen at run time; the
+      // scheduling fences keep the pieces from overlapping (this path is rare and must stay light)
+      const int j0 = n * BN;
+      const bool more = n + 1 < n_tiles;
+      const bool n8 = (rb1 >> my_rl) & 1u;
+      const char* vst = vbuf + (n & 1) * L::VSTAGE;
+      const char* kst = kbuf + ((n + 1) & 1) * L::KSTAGE;
+      const float* scl_n1 = scl_of(slot_next());
+      // each half settles before the P.V of the half before it, so its slow path also rescales
+      // that half's pending P
+      if (n >= n_full) wv.template mask<1>(j0 + 32);
+      wv.template settle<1, 0>(wv.template softmax<1>());
+      __builtin_amdgcn_sched_barrier(0);
+      wv.template pv<0>(vst);
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) {
+        if (n8) qk_tile<0, true, DUMP>(wv, kst, q16w, scl_n1, j0 + BN, dc);
+        else qk_tile<0, false, DUMP>(wv, kst, q16w, scl_n1, j0 + BN, dc);
+        __builtin_amdgcn_sched_barrier(0);
+        if (n + 1 >= n_full) wv.template mask<0>(j0 + BN);
+        wv.template settle<0, 1>(wv.template softmax<0>());
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      wv.template pv<1>(vst);
+      if (more) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (n8) qk_tile<1, true, DUMP>(wv, kst, q16w, scl_n1, j0 + BN, dc);
+        else qk_tile<1, false, DUMP>(wv, kst, q16w, scl_n1, j0 + BN, dc);
+      }
+    }
+    end_iter();
+    ++n;
   }
 
   // ---- epilogue: O = O^T / l, LSE = (m + log2 l) * ln 2
-  if (!row_valid) return;
-  const int64_t tq = q_begin + my_q;
-  const float inv_l = l_i > 0.0f ? 1.0f / l_i : 0.0f;
+  const float l_row = wv.l + __shfl_xor(wv.l, 32);
+  if (!wv.row_valid) return;
+  const int64_t tq = q_begin + wv.my_q;
+  const float inv_l = l_row > 0.0f ? 1.0f / l_row : 0.0f;
   if (a.out_f32) {
     float* op = static_cast<float*>(a.out) + (tq * a.hq + h) * D;
 #pragma unroll
@@ -383,7 +658,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
       for (int g4 = 0; g4 < 4; ++g4) {
         float4v v4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = o[dblk][4 * g4 + e] * inv_l;
+        for (int e = 0; e < 4; ++e) v4[e] = wv.o[dblk][4 * g4 + e] * inv_l;
         *reinterpret_cast<float4v*>(op + dblk * 32 + 8 * g4 + 4 * hl) = v4;
       }
   } else {
@@ -394,13 +669,13 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
       for (int g4 = 0; g4 < 4; ++g4) {
         half4v v4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = static_cast<_Float16>(o[dblk][4 * g4 + e] * inv_l);
+        for (int e = 0; e < 4; ++e) v4[e] = static_cast<_Float16>(wv.o[dblk][4 * g4 + e] * inv_l);
         *reinterpret_cast<half4v*>(op + dblk * 32 + 8 * g4 + 4 * hl) = v4;
       }
   }
   if (a.lse != nullptr && hl == 0)
     a.lse[static_cast<int64_t>(h) * a.total_q + tq] =
-        l_i > 0.0f ? (m_i + log2f(l_i)) * 0.69314718055994531f : -INFINITY;
+        l_row > 0.0f ? (wv.m_use + log2f(l_row)) * 0.69314718055994531f : -INFINITY;
 }
 
 template <int D, bool KV8>
@@ -408,7 +683,11 @@ hipError_t launch_t(const FwdArgs& a, int32_t batch, hipStream_t stream) {
   const int n_ct = (a.max_seqlen_q + BM - 1) / BM;
   if (n_ct == 0 || batch == 0) return hipSuccess;
   dim3 grid(static_cast<unsigned>(a.hq), static_cast<unsigned>(n_ct), static_cast<unsigned>(batch));
-  prefill_fwd_kernel<D, KV8><<<grid, dim3(NW * 64), 0, stream>>>(a);
+  // the debug dump of the INT8 accumulators is compiled into a separate instance of the kernel
+  if (a.dump != nullptr)
+    prefill_fwd_kernel<D, KV8, true><<<grid, dim3(NW * 64), 0, stream>>>(a);
+  else
+    prefill_fwd_kernel<D, KV8, false><<<grid, dim3(NW * 64), 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -151,11 +151,13 @@ def test_workspace_size(lib):
     p = base_params()
     n = ctypes.c_int64(0)
     assert lib.tilemix_prefill_workspace_size(ctypes.byref(p), ctypes.byref(n)) == B.TILEMIX_OK
-    # V^T tiles: hkv * (ceil(total_k / 64) + batch) tiles of 64 x head_dim fp16
-    assert n.value == 2 * (256 // 64 + 1) * 64 * 128 * 2
+    # hkv * (ceil(total_k / 64) + batch) tiles, each 64 x head_dim fp16 of V^T and 2 x 64 fp32
+    # per-key score factors
+    tiles = 2 * (256 // 64 + 1)
+    assert n.value == tiles * 64 * 128 * 2 + tiles * 2 * 64 * 4
     p.kv_int8 = 1
     assert lib.tilemix_prefill_workspace_size(ctypes.byref(p), ctypes.byref(n)) == B.TILEMIX_OK
-    assert n.value == 2 * 5 * 64 * 128 * 2 + 256 * 2 * 128 * 2
+    assert n.value == tiles * 64 * 128 * 2 + tiles * 2 * 64 * 4 + 256 * 2 * 128 * 2
     p.head_dim = 80
     assert lib.tilemix_prefill_workspace_size(ctypes.byref(p), ctypes.byref(n)) == B.TILEMIX_EUNSUPPORTED
     assert lib.tilemix_prefill_workspace_size(None, ctypes.byref(n)) == B.TILEMIX_EINVAL

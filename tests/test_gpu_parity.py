@@ -186,6 +186,21 @@ def test_outlier_channels_and_scale_override():
     check_lse(prob.lse.cpu().numpy(), ref_lse, "lse")
 
 
+@pytest.mark.parametrize("route", [None, "fp16", "int8"])
+def test_rising_scores_rescale_paths(route):
+    """Key norms grow along the sequence, so the running max keeps rising and the lazy-rescale slow
+    path fires in the middle of the key loop, including while the P of the previous key half is
+    still pending (route changes and FP16 runs take the generic iteration)."""
+    w = wl.custom(seqlens=[1100, 700], hq=4, hk=2, d=128, bm_r=128, bn_r=128, group=1, seed=31,
+                  route=route, p_fp16=0.5)
+    growth = (1.0 + np.arange(w.total, dtype=np.float32) / 96.0)[:, None, None]
+    w.k = (w.k.astype(np.float32) * growth).astype(np.float16)
+    prob = run(w)
+    ref, ref_lse, _, _ = oracle.prepare(w).prefill()
+    check_out(prob.out.cpu().numpy(), ref, "out")
+    check_lse(prob.lse.cpu().numpy(), ref_lse, "lse")
+
+
 def test_bottom_right_causal_unequal_lengths():
     rng = np.random.default_rng(23)
     Lq, Lk, hq, hk, d, bm, bn = 40, 300, 2, 1, 128, 32, 64
