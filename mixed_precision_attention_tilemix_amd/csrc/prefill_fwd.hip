@@ -92,6 +92,15 @@ __device__ __forceinline__ void dma16(const void* src, char* lds_block) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_block, 16, 0, 0);
 }
 
+// Barrier after direct global->LDS loads. The memory fence of a workgroup barrier does not
+// cover the LDS writes of these loads (the compiler does not count them as LDS stores), so each
+// wave first waits for all of its own outstanding loads (s_waitcnt with every counter at zero);
+// after the barrier every wave's loads have landed.
+__device__ __forceinline__ void dma_barrier() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
 // Row index inside a 32-key block that MFMA row r reads: bits 2 and 3 swapped.
 __device__ __forceinline__ int perm32(int r) { return (r & 0x13) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
@@ -110,14 +119,16 @@ struct Stager {
   static constexpr int I8 = (NB8 + NW - 1) / NW;
   static constexpr int IV = (NBV + NW - 1) / NW;
 
-  // Uniform byte pointers (scalar registers); the small per-lane byte offsets are recomputed at
-  // every issue from an opaque copy of the lane id (a few VALU operations) rather than kept live.
+  // Uniform byte pointers (scalar registers) and per-lane byte offsets of this wave's blocks
+  // inside a full tile (vector registers), so that a direct load is one scalar-base +
+  // 32-bit-offset instruction; only the partial last tile of a sequence recomputes clamped rows.
   const char* k16;   // key 0 of the sequence, this KV head, fp16 K
   const char* k8;    // the same, int8 K
   const char* vt;    // V^T tile 0
   const char* ks;    // factors of tile 0
   int64_t st16;      // bytes between consecutive keys, fp16 K
   int64_t st8;       // bytes between consecutive keys, int8 K
+  uint32_t o16[I16], o8[I8], ov;
   int w, Lk;
 
   __device__ void init(const FwdArgs& a, int k_begin, int hk, int Lk_, int w_, int64_t tile0) {
@@ -129,27 +140,37 @@ struct Stager {
     k8 = reinterpret_cast<const char*>(a.k8) + static_cast<int64_t>(k_begin) * st8 + static_cast<int64_t>(hk) * D;
     vt = reinterpret_cast<const char*>(a.vt + tile0 * (D * BN));
     ks = reinterpret_cast<const char*>(a.ks + tile0 * (2 * BN));
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < I16; ++i) o16[i] = off16(lane, i, BN);
+#pragma unroll
+    for (int i = 0; i < I8; ++i) o8[i] = off8(lane, i, BN);
+    ov = static_cast<uint32_t>(lane * 16);
   }
-  __device__ static int opaque_lane() {
-    int l = threadIdx.x & 63;
-    asm volatile("" : "+v"(l));
-    return l;
+  // byte offset of the chunk that lane loads in its i-th block of a tile whose rows past `last`
+  // repeat row `last`
+  __device__ uint32_t off16(int lane, int i, int last) const {
+    const int row = (w + NW * i) * R16 + lane / L::C16;
+    return static_cast<uint32_t>(min(row, last) * st16) + ((lane % L::C16) ^ L::f16(row)) * 16;
+  }
+  __device__ uint32_t off8(int lane, int i, int last) const {
+    const int row = (w + NW * i) * R8 + lane / L::C8;
+    return static_cast<uint32_t>(min(row, last) * st8) + ((lane % L::C8) ^ L::f8(row)) * 16;
   }
 
   // K tile n into stage buf: fp16 rows if need16, int8 rows if need8. Rows past the sequence
   // end repeat the last key; the kernel masks them before use.
   __device__ __forceinline__ void k_tile(char* buf, int n, bool need16, bool need8) const {
+    __builtin_assume(w >= 0 && w < NW);
     const int j0 = n * BN;
-    const int last = Lk - 1 - j0;  // rows beyond it repeat it
-    const int lane = opaque_lane();
+    const bool tail = j0 + BN > Lk;
+    const int lane = threadIdx.x & 63;
     if (need16) {
       const char* base = k16 + static_cast<int64_t>(j0) * st16;
 #pragma unroll
       for (int i = 0; i < I16; ++i) {
         if (w + NW * i >= NB16) break;
-        const int row = (w + NW * i) * R16 + lane / L::C16;
-        const uint32_t chunk = ((lane % L::C16) ^ L::f16(row)) * 16;
-        dma16(base + (static_cast<uint32_t>(min(row, last) * st16) + chunk), buf + L::K16 + (w + NW * i) * 1024);
+        dma16(base + (tail ? off16(lane, i, Lk - 1 - j0) : o16[i]), buf + L::K16 + (w + NW * i) * 1024);
       }
     }
     if (need8) {
@@ -157,29 +178,25 @@ struct Stager {
 #pragma unroll
       for (int i = 0; i < I8; ++i) {
         if (w + NW * i >= NB8) break;
-        const int row = (w + NW * i) * R8 + lane / L::C8;
-        const uint32_t chunk = ((lane % L::C8) ^ L::f8(row)) * 16;
-        dma16(base + (static_cast<uint32_t>(min(row, last) * st8) + chunk), buf + L::K8 + (w + NW * i) * 1024);
+        dma16(base + (tail ? off8(lane, i, Lk - 1 - j0) : o8[i]), buf + L::K8 + (w + NW * i) * 1024);
       }
     }
   }
 
   // Pre-transposed V^T tile n (contiguous in the workspace) into stage buf.
   __device__ __forceinline__ void v_tile(char* buf, int n) const {
+    __builtin_assume(w >= 0 && w < NW);
     const char* src = vt + static_cast<int64_t>(n) * (D * BN * 2);
-    const uint32_t lo = static_cast<uint32_t>(opaque_lane() * 16);
 #pragma unroll
     for (int i = 0; i < IV; ++i) {
       if (w + NW * i >= NBV) break;
-      dma16(src + (w + NW * i) * 1024 + lo, buf + (w + NW * i) * 1024);
+      dma16(src + (w + NW * i) * 1024 + ov, buf + (w + NW * i) * 1024);
     }
   }
 
   // The 512 bytes of per-key factors of tile n into a factor slot.
   __device__ __forceinline__ void scales(char* buf, int n) const {
-    const int lane = opaque_lane();
-    if (w == NW - 1 && lane < 32)
-      dma16(ks + static_cast<int64_t>(n) * (2 * BN * 4) + static_cast<uint32_t>(lane * 16), buf);
+    if (w == NW - 1 && (threadIdx.x & 63) < 32) dma16(ks + static_cast<int64_t>(n) * (2 * BN * 4) + ov, buf);
   }
 };
 
@@ -221,13 +238,16 @@ struct Wave {
   half8v p[2][2];      // fp16 P of the two key halves, [half][16-key step]
   float m, m_use, l;   // running max (log2 units), its finite stand-in, this lane's row sum
 
-  // s[KB] = scores of key half KB of the K tile in stage kst; scl = that tile's per-key factors.
+  // s[KB] = raw scores of key half KB of the K tile in stage kst: int32 accumulators (as bits)
+  // for INT8, fp32 dot products for FP16; convert<KB, I8>() turns them into scores.
   // With DUMP, the raw int32 accumulators of an INT8 half also go to the debug dump when
   // dump_row is not NULL: key j of this lane's query row is dump_row[(j / bn_r) * tile_stride +
   // j % bn_r], for the keys j < Lk; key0 = sequence-local index of the half's first key.
-  template <int KB, bool I8, bool DUMP>
-  __device__ __forceinline__ void qk(const char* kst, const char* q16, const float* scl, int32_t* dump_row,
-                                     int key0, int Lk, int bn_r, int tile_stride) {
+  // FENCED: the call sits alone between scheduling fences (the generic iteration), and the FP16
+  // chain is split by one more fence so that fewer operands are in flight.
+  template <int KB, bool I8, bool DUMP, bool FENCED = false>
+  __device__ __forceinline__ void qk(const char* kst, const char* q16, int32_t* dump_row, int key0, int Lk,
+                                     int bn_r, int tile_stride) {
     using L = Smem<D>;
     if constexpr (I8) {
       int16v acc = kBiasedI8 ? bias : int16v{};
@@ -245,49 +265,47 @@ struct Wave {
           }
         }
       }
+      s[KB] = __builtin_bit_cast(float16v, acc);
+    } else {
+      float16v acc = {};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        // fenced: at most half of the chain's operands in flight
+        if (FENCED && ks == D / 32) __builtin_amdgcn_sched_barrier(0);
+        const half8v qv = *reinterpret_cast<const half8v*>(q16 + (qbase16 ^ (32 * ks)));
+        const half8v kf = *reinterpret_cast<const half8v*>(kst + L::K16 + KB * 32 * L::RB16 + (kbase16 ^ (32 * ks)));
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qv, acc, 0, 0, 0);
+      }
+      s[KB] = acc;
+    }
+  }
+
+  // Raw scores of half KB -> fp32 scores in units of 1 / c[KB]; scl = the per-key factors of the
+  // half's tile. INT8: dk' * (q8 . k8); FP16: the dot product (times dk' for an INT8 cache).
+  template <int KB, bool I8>
+  __device__ __forceinline__ void convert(const float* scl) {
+    if constexpr (I8 || KV8) {
 #pragma unroll
       for (int g8 = 0; g8 < 2; ++g8) {
         const int kidx = 32 * KB + 16 * g8 + 8 * hl;
         const float4v d0 = *reinterpret_cast<const float4v*>(scl + kidx);
         const float4v d1 = *reinterpret_cast<const float4v*>(scl + kidx + 4);
         float4v b0 = {}, b1 = {};
-        if constexpr (kBiasedI8) {
+        if constexpr (I8 && kBiasedI8) {
           b0 = *reinterpret_cast<const float4v*>(scl + BN + kidx);
           b1 = *reinterpret_cast<const float4v*>(scl + BN + kidx + 4);
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float dk = e < 4 ? d0[e] : d1[e - 4];
-          if constexpr (kBiasedI8)
-            s[KB][8 * g8 + e] = __builtin_fmaf(__builtin_bit_cast(float, acc[8 * g8 + e]), dk, e < 4 ? b0[e] : b1[e - 4]);
-          else
-            s[KB][8 * g8 + e] = static_cast<float>(acc[8 * g8 + e]) * dk;
+          const float v = s[KB][8 * g8 + e];
+          if constexpr (!I8) s[KB][8 * g8 + e] = v * dk;
+          else if constexpr (kBiasedI8) s[KB][8 * g8 + e] = __builtin_fmaf(v, dk, e < 4 ? b0[e] : b1[e - 4]);
+          else s[KB][8 * g8 + e] = static_cast<float>(__builtin_bit_cast(int, v)) * dk;
         }
       }
-      c[KB] = cq;
-    } else {
-      float16v acc = {};
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const half8v qv = *reinterpret_cast<const half8v*>(q16 + (qbase16 ^ (32 * ks)));
-        const half8v kf = *reinterpret_cast<const half8v*>(kst + L::K16 + KB * 32 * L::RB16 + (kbase16 ^ (32 * ks)));
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qv, acc, 0, 0, 0);
-      }
-      if constexpr (KV8) {
-        // K of the INT8 cache enters the FP16 path as exact fp16(k8): apply its scale here
-#pragma unroll
-        for (int g8 = 0; g8 < 2; ++g8) {
-          const int kidx = 32 * KB + 16 * g8 + 8 * hl;
-          const float4v d0 = *reinterpret_cast<const float4v*>(scl + kidx);
-          const float4v d1 = *reinterpret_cast<const float4v*>(scl + kidx + 4);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) s[KB][8 * g8 + e] = acc[8 * g8 + e] * (e < 4 ? d0[e] : d1[e - 4]);
-        }
-      } else {
-        s[KB] = acc;
-      }
-      c[KB] = cs;
     }
+    c[KB] = I8 ? cq : cs;
   }
 
   // Legality mask of half KB (causal diagonal, sequence tail): illegal scores become -inf.
@@ -395,25 +413,34 @@ struct DumpCtx {
 
 // Scores of half KB of the tile at key j0 with the route chosen by I8 (and the dump, if any).
 template <int KB, bool I8, bool DUMP, int D, bool KV8>
-__device__ __forceinline__ void qk_tile(Wave<D, KV8>& wv, const char* kst, const char* q16, const float* scl,
-                                        int j0, const DumpCtx& dc) {
+__device__ __forceinline__ void qk_tile(Wave<D, KV8>& wv, const char* kst, const char* q16, int j0,
+                                        const DumpCtx& dc) {
   int32_t* row = (DUMP && I8 && j0 <= dc.act_limit) ? dc.row : nullptr;
-  wv.template qk<KB, I8, DUMP>(kst, q16, scl, row, j0 + 32 * KB, dc.Lk, dc.bn_r, dc.tile_stride);
+  wv.template qk<KB, I8, DUMP, true>(kst, q16, row, j0 + 32 * KB, dc.Lk, dc.bn_r, dc.tile_stride);
+}
+
+// convert<KB, I8>() with the route chosen at run time.
+template <int KB, int D, bool KV8>
+__device__ __forceinline__ void convert_rt(Wave<D, KV8>& wv, bool i8, const float* scl) {
+  if (i8) wv.template convert<KB, true>(scl);
+  else wv.template convert<KB, false>(scl);
 }
 
 // One main-loop iteration of a run whose tiles n and n+1 share this wave's route I8 and need no
-// mask: the softmax of a key half overlaps the P.V of the previous half and the score MFMAs of
-// the next one, in straight-line code apart from the rare slow path.
+// mask: the score conversion and softmax of a key half overlap the P.V of the previous half and
+// the score MFMAs of the next one, in straight-line code apart from the rare slow path.
 template <int D, bool KV8, bool I8>
 __device__ __forceinline__ void run_iter(Wave<D, KV8>& wv, const char* vst, const char* kst, const char* q16,
-                                         const float* scl_n1) {
+                                         const float* scl_n, const float* scl_n1) {
+  wv.template convert<1, I8>(scl_n);
   float rs = wv.template softmax<1>();
   wv.template pv<0>(vst);
-  wv.template qk<0, I8, false>(kst, q16, scl_n1, nullptr, 0, 0, 1, 0);
+  wv.template qk<0, I8, false>(kst, q16, nullptr, 0, 0, 1, 0);
   wv.template settle<1>(rs);
+  wv.template convert<0, I8>(scl_n1);
   rs = wv.template softmax<0>();
   wv.template pv<1>(vst);
-  wv.template qk<1, I8, false>(kst, q16, scl_n1, nullptr, 0, 0, 1, 0);
+  wv.template qk<1, I8, false>(kst, q16, nullptr, 0, 0, 1, 0);
   wv.template settle<0>(rs);
 }
 
@@ -545,17 +572,19 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
     stg.k_tile(kbuf + L::KSTAGE, 1, rb1 != full, rb1 != 0u);
     stg.scales(sbuf + L::SSLOT, 1);
   }
-  __syncthreads();
+  dma_barrier();  // also publishes the fp16 Q stores
 
   if (wave_live && n_tiles > 0) {
     const float* scl0 = reinterpret_cast<const float*>(sbuf);
-    if ((rb0 >> my_rl) & 1u) {
-      qk_tile<0, true, DUMP>(wv, kbuf, q16w, scl0, 0, dc);
-      qk_tile<1, true, DUMP>(wv, kbuf, q16w, scl0, 0, dc);
+    const bool i8 = (rb0 >> my_rl) & 1u;
+    if (i8) {
+      qk_tile<0, true, DUMP>(wv, kbuf, q16w, 0, dc);
+      qk_tile<1, true, DUMP>(wv, kbuf, q16w, 0, dc);
     } else {
-      qk_tile<0, false, DUMP>(wv, kbuf, q16w, scl0, 0, dc);
-      qk_tile<1, false, DUMP>(wv, kbuf, q16w, scl0, 0, dc);
+      qk_tile<0, false, DUMP>(wv, kbuf, q16w, 0, dc);
+      qk_tile<1, false, DUMP>(wv, kbuf, q16w, 0, dc);
     }
+    convert_rt<0>(wv, i8, scl0);
     if (n_full < 1) wv.template mask<0>(0);
     wv.template settle<0>(wv.template softmax<0>());
   }
@@ -570,7 +599,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
 
   // barrier, then the direct loads of K_{n+2}, its factors and V_{n+1}; route bits of tile n+3
   auto begin_iter = [&](int n) {
-    __syncthreads();  // K_{n+1}, V_n and their factors landed; stages of K_n and V_{n-1} free
+    dma_barrier();  // K_{n+1}, V_n and their factors landed; stages of K_n and V_{n-1} free
     if (n + 2 < n_tiles) {
       stg.k_tile(kbuf + (n & 1) * L::KSTAGE, n + 2, rb2 != full, rb2 != 0u);
       stg.scales(sbuf + (slot_n == 0 ? 2 : slot_n - 1) * L::SSLOT, n + 2);
@@ -591,7 +620,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
   };
   // iteration n can take the specialised loop: tiles n and n+1 exist, are both INT8-routed for
   // this wave and need no mask (FP16 runs take the generic iteration, which keeps the register
-  // footprint of the kernel within two waves per SIMD without spills)
+  // footprint of the kernel within two waves per SIMD)
   auto fast = [&](int n) {
     return fast_ok && n + 1 < n_tiles && n + 1 < n_full && (((rb0 & rb1) >> my_rl) & 1u) != 0u;
   };
@@ -603,7 +632,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
       do {
         begin_iter(n);
         run_iter<D, KV8, true>(wv, vbuf + (n & 1) * L::VSTAGE, kbuf + ((n + 1) & 1) * L::KSTAGE, q16w,
-                               scl_of(slot_next()));
+                               scl_of(slot_n), scl_of(slot_next()));
         end_iter();
         ++n;
       } while (fast(n));
@@ -621,15 +650,18 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
       const float* scl_n1 = scl_of(slot_next());
       // each half settles before the P.V of the half before it, so its slow path also rescales
       // that half's pending P
+      const bool c8 = (rb0 >> my_rl) & 1u;
+      convert_rt<1>(wv, c8, scl_of(slot_n));
       if (n >= n_full) wv.template mask<1>(j0 + 32);
       wv.template settle<1, 0>(wv.template softmax<1>());
       __builtin_amdgcn_sched_barrier(0);
       wv.template pv<0>(vst);
       __builtin_amdgcn_sched_barrier(0);
       if (more) {
-        if (n8) qk_tile<0, true, DUMP>(wv, kst, q16w, scl_n1, j0 + BN, dc);
-        else qk_tile<0, false, DUMP>(wv, kst, q16w, scl_n1, j0 + BN, dc);
+        if (n8) qk_tile<0, true, DUMP>(wv, kst, q16w, j0 + BN, dc);
+        else qk_tile<0, false, DUMP>(wv, kst, q16w, j0 + BN, dc);
         __builtin_amdgcn_sched_barrier(0);
+        convert_rt<0>(wv, n8, scl_n1);
         if (n + 1 >= n_full) wv.template mask<0>(j0 + BN);
         wv.template settle<0, 1>(wv.template softmax<0>());
         __builtin_amdgcn_sched_barrier(0);
@@ -637,8 +669,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
       wv.template pv<1>(vst);
       if (more) {
         __builtin_amdgcn_sched_barrier(0);
-        if (n8) qk_tile<1, true, DUMP>(wv, kst, q16w, scl_n1, j0 + BN, dc);
-        else qk_tile<1, false, DUMP>(wv, kst, q16w, scl_n1, j0 + BN, dc);
+        if (n8) qk_tile<1, true, DUMP>(wv, kst, q16w, j0 + BN, dc);
+        else qk_tile<1, false, DUMP>(wv, kst, q16w, j0 + BN, dc);
       }
     }
     end_iter();

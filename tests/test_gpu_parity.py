@@ -259,6 +259,33 @@ def test_deterministic():
     assert torch.equal(o1, a.out) and torch.equal(l1, a.lse)
 
 
+@pytest.mark.parametrize("name", ["varlen64k", "mha8k"])
+def test_deterministic_full_size(name):
+    """Bitwise identical outputs run to run, for the production kernel and for the instance with
+    the debug dump compiled in (which takes the generic iteration everywhere): the staged K/V
+    tiles must have landed in LDS before any wave reads them."""
+    w = named(name)
+    prob = DeviceProblem(w)
+    runs = []
+    for _ in range(3):
+        prob.out.fill_(float("nan"))
+        prob.step()
+        torch.cuda.synchronize()
+        runs.append(prob.out.clone())
+    for r in runs[1:]:
+        assert torch.equal(r, runs[0]), f"{name}: production kernel not deterministic"
+    ntiles = -(-max(w.seqlens) // w.bn_r)
+    dump = torch.full((1, ntiles, w.bm_r, w.bn_r), SENTINEL, dtype=torch.int32, device="cuda")
+    gen = []
+    for _ in range(3):
+        prob.out.fill_(float("nan"))
+        prob.attention(debug_s32=dump, debug_head=0, debug_mtile_begin=0, debug_mtile_count=1)
+        torch.cuda.synchronize()
+        gen.append(prob.out.clone())
+    for r in gen[1:]:
+        assert torch.equal(r, gen[0]), f"{name}: dump instance not deterministic"
+
+
 # ----------------------------------------------------------------------------- int32 tiles
 
 def compare_dump(w, prob, head, m0, mcount):
