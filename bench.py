@@ -30,6 +30,41 @@ PEAK_INT8 = 5033.2   # TOP/s, dense INT8 MFMA
 PEAK_HBM = 8000.0    # GB/s
 
 WORKLOAD = "gqa32k"
+CAL_BYTES = 256 << 20   # plain device copy of known size: calibrates the HBM byte counters
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_fwd_gqa32k_traffic.md")
+KERNEL_SRC = os.path.join(ROOT, "mixed_precision_attention_tilemix_amd", "csrc", "prefill_fwd.hip")
+
+
+def calibration_copy():
+    """One plain device-to-device copy of CAL_BYTES (read CAL_BYTES, write CAL_BYTES), so that a
+    rocprofv3 --pmc run of this script sees what FETCH_SIZE / WRITE_SIZE report for known bytes."""
+    import torch
+    src = torch.full((CAL_BYTES,), 1, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def measured_traffic():
+    """HBM bytes per fused-kernel launch from the committed counter summary, or None when the
+    summary is missing or was taken on a different kernel source."""
+    import hashlib
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    digest = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    fields = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and line.strip().startswith("- "):
+            k, v = line.strip()[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_source_sha256") != digest:
+        return None
+    try:
+        return float(fields["fetch_bytes_per_launch"]) + float(fields["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def int8_pair_counts(w):
@@ -97,6 +132,7 @@ def main():
     from mixed_precision_attention_tilemix_amd.runner import DeviceProblem
 
     binding.load()
+    calibration_copy()
     w = workloads.make(args.workload)
     prob = DeviceProblem(w, out_dtype=torch.float16)
     stream = torch.cuda.current_stream()
@@ -160,13 +196,13 @@ def main():
         "quantize_pack_ms": round(pre_ms, 4),
         "quantize_gbps": round(q_bytes / (pre_ms * 1e-3) / 1e9, 1),
         "roofline": {
-            "kernel": "prefill_fwd_kernel<128,NW,false>",
+            "kernel": "prefill_fwd_kernel<128, false, false> (+ vt_pack pre-pass in the timed call)",
             "bound": "mfma",
             "achieved": round(fwd_tflops, 2),
             "peak": round(peak_mixed, 1),
             "unit": "TFLOP/s",
             "frac": round(fwd_tflops / peak_mixed, 4),
-            "traffic": None,
+            "traffic": measured_traffic() if args.workload == WORKLOAD else None,
             "flops_per_launch": flops,
             "peak_note": f"mixed MFMA peak for INT8 fraction {r:.4f}: INT8 QK^T at {PEAK_INT8}, "
                          f"FP16 QK^T and P.V at {PEAK_FP16} TFLOP/s",
