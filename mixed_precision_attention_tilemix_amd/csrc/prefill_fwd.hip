@@ -119,21 +119,27 @@ struct Stager {
   static constexpr int I8 = (NB8 + NW - 1) / NW;
   static constexpr int IV = (NBV + NW - 1) / NW;
 
-  // Uniform byte pointers (scalar registers) and per-lane byte offsets of this wave's blocks
-  // inside a full tile (vector registers), so that a direct load is one scalar-base +
-  // 32-bit-offset instruction; only the partial last tile of a sequence recomputes clamped rows.
-  const char* k16;   // key 0 of the sequence, this KV head, fp16 K
-  const char* k8;    // the same, int8 K
-  const char* vt;    // V^T tile 0
-  const char* ks;    // factors of tile 0
+  // Uniform byte pointers (scalar registers) to the next tile of each stream, and per-lane byte
+  // offsets of this wave's blocks inside a full tile (vector registers), so that a direct load is
+  // one scalar-base + 32-bit-offset instruction and advancing a stream is one pointer add; only
+  // the partial last tile of a sequence recomputes clamped rows. Each stream is consumed in tile
+  // order, one call per tile.
+  const char* k16;   // next K tile, fp16 rows
+  const char* k8;    // next K tile, int8 rows
+  const char* vt;    // next V^T tile
+  const char* ks;    // factors of the next factor tile
   int64_t st16;      // bytes between consecutive keys, fp16 K
   int64_t st8;       // bytes between consecutive keys, int8 K
   uint32_t o16[I16], o8[I8], ov;
   int w, Lk;
+  int kn;            // index of the next K tile
+  int kfull;         // K tiles [0, kfull) are whole
 
   __device__ void init(const FwdArgs& a, int k_begin, int hk, int Lk_, int w_, int64_t tile0) {
     w = w_;
     Lk = Lk_;
+    kn = 0;
+    kfull = Lk / BN;
     st16 = a.k_stride_tok * 2;
     st8 = static_cast<int64_t>(a.hkv) * D;
     k16 = reinterpret_cast<const char*>(a.k) + k_begin * st16 + hk * a.k_stride_head * 2;
@@ -158,45 +164,53 @@ struct Stager {
     return static_cast<uint32_t>(min(row, last) * st8) + ((lane % L::C8) ^ L::f8(row)) * 16;
   }
 
-  // K tile n into stage buf: fp16 rows if need16, int8 rows if need8. Rows past the sequence
-  // end repeat the last key; the kernel masks them before use.
-  __device__ __forceinline__ void k_tile(char* buf, int n, bool need16, bool need8) const {
+  // The next K tile into stage buf: fp16 rows if need16, int8 rows if need8. Rows past the
+  // sequence end repeat the last key; the kernel masks them before use.
+  __device__ __forceinline__ void k_next(char* buf, bool need16, bool need8) {
     __builtin_assume(w >= 0 && w < NW);
-    const int j0 = n * BN;
-    const bool tail = j0 + BN > Lk;
     const int lane = threadIdx.x & 63;
-    if (need16) {
-      const char* base = k16 + static_cast<int64_t>(j0) * st16;
+    if (__builtin_expect(kn < kfull, 1)) {
+      if (need16) {
 #pragma unroll
-      for (int i = 0; i < I16; ++i) {
-        if (w + NW * i >= NB16) break;
-        dma16(base + (tail ? off16(lane, i, Lk - 1 - j0) : o16[i]), buf + L::K16 + (w + NW * i) * 1024);
+        for (int i = 0; i < I16; ++i)
+          if (w + NW * i < NB16) dma16(k16 + o16[i], buf + L::K16 + (w + NW * i) * 1024);
+      }
+      if (need8) {
+#pragma unroll
+        for (int i = 0; i < I8; ++i)
+          if (w + NW * i < NB8) dma16(k8 + o8[i], buf + L::K8 + (w + NW * i) * 1024);
+      }
+    } else {
+      const int last = Lk - 1 - kn * BN;
+      if (need16) {
+#pragma unroll
+        for (int i = 0; i < I16; ++i)
+          if (w + NW * i < NB16) dma16(k16 + off16(lane, i, last), buf + L::K16 + (w + NW * i) * 1024);
+      }
+      if (need8) {
+#pragma unroll
+        for (int i = 0; i < I8; ++i)
+          if (w + NW * i < NB8) dma16(k8 + off8(lane, i, last), buf + L::K8 + (w + NW * i) * 1024);
       }
     }
-    if (need8) {
-      const char* base = k8 + static_cast<int64_t>(j0) * st8;
-#pragma unroll
-      for (int i = 0; i < I8; ++i) {
-        if (w + NW * i >= NB8) break;
-        dma16(base + (tail ? off8(lane, i, Lk - 1 - j0) : o8[i]), buf + L::K8 + (w + NW * i) * 1024);
-      }
-    }
+    k16 += BN * st16;
+    k8 += BN * st8;
+    ++kn;
   }
 
-  // Pre-transposed V^T tile n (contiguous in the workspace) into stage buf.
-  __device__ __forceinline__ void v_tile(char* buf, int n) const {
+  // The next pre-transposed V^T tile (contiguous in the workspace) into stage buf.
+  __device__ __forceinline__ void v_next(char* buf) {
     __builtin_assume(w >= 0 && w < NW);
-    const char* src = vt + static_cast<int64_t>(n) * (D * BN * 2);
 #pragma unroll
-    for (int i = 0; i < IV; ++i) {
-      if (w + NW * i >= NBV) break;
-      dma16(src + (w + NW * i) * 1024 + ov, buf + (w + NW * i) * 1024);
-    }
+    for (int i = 0; i < IV; ++i)
+      if (w + NW * i < NBV) dma16(vt + (w + NW * i) * 1024 + ov, buf + (w + NW * i) * 1024);
+    vt += D * BN * 2;
   }
 
-  // The 512 bytes of per-key factors of tile n into a factor slot.
-  __device__ __forceinline__ void scales(char* buf, int n) const {
-    if (w == NW - 1 && (threadIdx.x & 63) < 32) dma16(ks + static_cast<int64_t>(n) * (2 * BN * 4) + ov, buf);
+  // The 512 bytes of per-key factors of the next factor tile into a factor slot.
+  __device__ __forceinline__ void s_next(char* buf) {
+    if (w == NW - 1 && (threadIdx.x & 63) < 32) dma16(ks + ov, buf);
+    ks += 2 * BN * 4;
   }
 };
 
@@ -564,13 +578,13 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
 
   // ---- prologue: K tiles 0 and 1, V^T tile 0, factors of tiles 0 and 1
   if (n_tiles > 0) {
-    stg.k_tile(kbuf, 0, rb0 != full, rb0 != 0u);
-    stg.v_tile(vbuf, 0);
-    stg.scales(sbuf, 0);
+    stg.k_next(kbuf, rb0 != full, rb0 != 0u);
+    stg.v_next(vbuf);
+    stg.s_next(sbuf);
   }
   if (n_tiles > 1) {
-    stg.k_tile(kbuf + L::KSTAGE, 1, rb1 != full, rb1 != 0u);
-    stg.scales(sbuf + L::SSLOT, 1);
+    stg.k_next(kbuf + L::KSTAGE, rb1 != full, rb1 != 0u);
+    stg.s_next(sbuf + L::SSLOT);
   }
   dma_barrier();  // also publishes the fp16 Q stores
 
@@ -601,10 +615,10 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
   auto begin_iter = [&](int n) {
     dma_barrier();  // K_{n+1}, V_n and their factors landed; stages of K_n and V_{n-1} free
     if (n + 2 < n_tiles) {
-      stg.k_tile(kbuf + (n & 1) * L::KSTAGE, n + 2, rb2 != full, rb2 != 0u);
-      stg.scales(sbuf + (slot_n == 0 ? 2 : slot_n - 1) * L::SSLOT, n + 2);
+      stg.k_next(kbuf + (n & 1) * L::KSTAGE, rb2 != full, rb2 != 0u);
+      stg.s_next(sbuf + (slot_n == 0 ? 2 : slot_n - 1) * L::SSLOT);
     }
-    if (n + 1 < n_tiles) stg.v_tile(vbuf + ((n + 1) & 1) * L::VSTAGE, n + 1);
+    if (n + 1 < n_tiles) stg.v_next(vbuf + ((n + 1) & 1) * L::VSTAGE);
     rb3 = rb2;
     if (++tig3 == tpg) {
       tig3 = 0;
