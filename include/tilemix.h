@@ -170,6 +170,35 @@ tilemix_status tilemix_prefill_workspace_size(const tilemix_fwd_params* params, 
  */
 tilemix_status tilemix_prefill_fwd(const tilemix_fwd_params* params, void* stream);
 
+/*
+ * tilemix_decode_workspace_size - bytes of device workspace tilemix_decode_fwd needs for these
+ * parameters (batch, hq, hkv, head_dim, max_seqlen_q and max_seqlen_k are read). Writes *bytes
+ * (0 when there is nothing to compute). Errors: EINVAL for NULL arguments, hq % hkv != 0 or
+ * negative sizes, EUNSUPPORTED for head_dim other than 64/128.
+ */
+tilemix_status tilemix_decode_workspace_size(const tilemix_fwd_params* params, int64_t* bytes);
+
+/*
+ * tilemix_decode_fwd - the same routed attention as tilemix_prefill_fwd (identical definition of
+ * s_ij, legality, route lookup, O and LSE) for a few new query tokens per sequence against a long
+ * INT8 K/V cache: the decode use of the INT8 cache interface (Section 4, "cache interface";
+ * Section 4.3 routed scores). With max_seqlen_q <= 8 every query of a sequence reads route row
+ * cu_mtiles[b] (route_block_m >= 32).
+ *
+ * Requirements beyond tilemix_prefill_fwd: kv_int8 = 1 (k, v NULL; k8, k_scale, v8, v_scale
+ * set), max_seqlen_q <= 8 and (hq / hkv) * max_seqlen_q <= 16 (EUNSUPPORTED otherwise),
+ * debug_s32 NULL (EINVAL), and a workspace of tilemix_decode_workspace_size() bytes,
+ * 256-byte aligned, owned by the caller (its contents on entry are irrelevant; calls that share
+ * it must not overlap in time). Scores, softmax and P.V are fp32 (P is not rounded to fp16);
+ * V_j = v_scale[j] * v8_j exactly.
+ *
+ * Implementation: a split-key pass (256 keys of one sequence and KV head per workgroup, every
+ * query row of that KV head's GQA group) writes per-chunk max / sum / unnormalised output into
+ * the workspace; a merge pass combines them into O and LSE. Both are enqueued on `stream`;
+ * the result is bitwise deterministic.
+ */
+tilemix_status tilemix_decode_fwd(const tilemix_fwd_params* params, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,7 +23,8 @@ TILEMIX_OK, TILEMIX_EINVAL, TILEMIX_EUNSUPPORTED, TILEMIX_ELAUNCH = 0, 1, 2, 3
 
 # The entry points declared in include/tilemix.h.
 EXPORTED = ("tilemix_last_error", "tilemix_version", "tilemix_quantize_qk",
-            "tilemix_pack_route_mask", "tilemix_prefill_workspace_size", "tilemix_prefill_fwd")
+            "tilemix_pack_route_mask", "tilemix_prefill_workspace_size", "tilemix_prefill_fwd",
+            "tilemix_decode_workspace_size", "tilemix_decode_fwd")
 
 
 class TilemixError(RuntimeError):
@@ -90,6 +91,10 @@ def load(path: Optional[str] = None):
     L.tilemix_prefill_workspace_size.argtypes = [ctypes.POINTER(FwdParams), ctypes.POINTER(ctypes.c_int64)]
     L.tilemix_prefill_fwd.restype = ctypes.c_int
     L.tilemix_prefill_fwd.argtypes = [ctypes.POINTER(FwdParams), vp]
+    L.tilemix_decode_workspace_size.restype = ctypes.c_int
+    L.tilemix_decode_workspace_size.argtypes = [ctypes.POINTER(FwdParams), ctypes.POINTER(ctypes.c_int64)]
+    L.tilemix_decode_fwd.restype = ctypes.c_int
+    L.tilemix_decode_fwd.argtypes = [ctypes.POINTER(FwdParams), vp]
     _lib = L
     return L
 
@@ -162,13 +167,10 @@ def tilemix_prefill_workspace_size(*, batch: int, hkv: int, head_dim: int, total
     return out.value
 
 
-def tilemix_prefill_fwd(*, q, q8, q_scale, k8, k_scale, route_words, cu_seqlens_q, cu_seqlens_k,
-                        cu_mtiles, max_seqlen_q: int, max_seqlen_k: int, route_block_m: int,
-                        route_block_n: int, route_group: int, out, workspace, k=None, v=None, v8=None,
-                        v_scale=None, causal: bool = True, softmax_scale: float = 0.0, lse=None,
-                        debug_s32=None, debug_head: int = 0, debug_mtile_begin: int = 0,
-                        debug_mtile_count: int = 0, stream=None) -> None:
-    """Fill tilemix_fwd_params from device tensors and call tilemix_prefill_fwd."""
+def _fwd_params(*, q, q8, q_scale, k8, k_scale, route_words, cu_seqlens_q, cu_seqlens_k,
+                cu_mtiles, max_seqlen_q, max_seqlen_k, route_block_m, route_block_n, route_group,
+                out, workspace, k, v, v8, v_scale, causal, softmax_scale, lse, debug_s32,
+                debug_head, debug_mtile_begin, debug_mtile_count) -> FwdParams:
     kv_int8 = v8 is not None
     qs = _tok_head_strides(q)
     ks = _tok_head_strides(k) if k is not None else (0, 0)
@@ -207,5 +209,51 @@ def tilemix_prefill_fwd(*, q, q8, q_scale, k8, k_scale, route_words, cu_seqlens_
         p.debug_head, p.debug_mtile_begin = debug_head, debug_mtile_begin
         p.debug_mtile_count, p.debug_ntiles_max = debug_mtile_count, debug_s32.shape[1]
     p.workspace = _ptr(workspace)
-    p.workspace_bytes = workspace.numel() * workspace.element_size()
+    p.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return p
+
+
+def tilemix_prefill_fwd(*, q, q8, q_scale, k8, k_scale, route_words, cu_seqlens_q, cu_seqlens_k,
+                        cu_mtiles, max_seqlen_q: int, max_seqlen_k: int, route_block_m: int,
+                        route_block_n: int, route_group: int, out, workspace, k=None, v=None, v8=None,
+                        v_scale=None, causal: bool = True, softmax_scale: float = 0.0, lse=None,
+                        debug_s32=None, debug_head: int = 0, debug_mtile_begin: int = 0,
+                        debug_mtile_count: int = 0, stream=None) -> None:
+    """Fill tilemix_fwd_params from device tensors and call tilemix_prefill_fwd."""
+    p = _fwd_params(q=q, q8=q8, q_scale=q_scale, k8=k8, k_scale=k_scale, route_words=route_words,
+                    cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k, cu_mtiles=cu_mtiles,
+                    max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k,
+                    route_block_m=route_block_m, route_block_n=route_block_n,
+                    route_group=route_group, out=out, workspace=workspace, k=k, v=v, v8=v8,
+                    v_scale=v_scale, causal=causal, softmax_scale=softmax_scale, lse=lse,
+                    debug_s32=debug_s32, debug_head=debug_head,
+                    debug_mtile_begin=debug_mtile_begin, debug_mtile_count=debug_mtile_count)
     _check(load().tilemix_prefill_fwd(ctypes.byref(p), _stream(stream)))
+
+
+def tilemix_decode_workspace_size(*, batch: int, hq: int, hkv: int, head_dim: int,
+                                  max_seqlen_q: int, max_seqlen_k: int) -> int:
+    """Bytes of device workspace tilemix_decode_fwd needs."""
+    p = FwdParams()
+    p.struct_size = ctypes.sizeof(FwdParams)
+    p.batch, p.hq, p.hkv, p.head_dim = batch, hq, hkv, head_dim
+    p.max_seqlen_q, p.max_seqlen_k = max_seqlen_q, max_seqlen_k
+    out = ctypes.c_int64(0)
+    _check(load().tilemix_decode_workspace_size(ctypes.byref(p), ctypes.byref(out)))
+    return out.value
+
+
+def tilemix_decode_fwd(*, q, q8, q_scale, k8, k_scale, v8, v_scale, route_words, cu_seqlens_q,
+                       cu_seqlens_k, cu_mtiles, max_seqlen_q: int, max_seqlen_k: int,
+                       route_block_m: int, route_block_n: int, route_group: int, out, workspace,
+                       causal: bool = True, softmax_scale: float = 0.0, lse=None,
+                       stream=None) -> None:
+    """Fill tilemix_fwd_params (INT8 K/V cache) from device tensors and call tilemix_decode_fwd."""
+    p = _fwd_params(q=q, q8=q8, q_scale=q_scale, k8=k8, k_scale=k_scale, route_words=route_words,
+                    cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k, cu_mtiles=cu_mtiles,
+                    max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k,
+                    route_block_m=route_block_m, route_block_n=route_block_n,
+                    route_group=route_group, out=out, workspace=workspace, k=None, v=None, v8=v8,
+                    v_scale=v_scale, causal=causal, softmax_scale=softmax_scale, lse=lse,
+                    debug_s32=None, debug_head=0, debug_mtile_begin=0, debug_mtile_count=0)
+    _check(load().tilemix_decode_fwd(ctypes.byref(p), _stream(stream)))

@@ -74,6 +74,112 @@ WorkspaceLayout workspace_layout(const tilemix_fwd_params* p) {
   return w;
 }
 
+// Bytes of the decode workspace: per (sequence, KV head, key chunk, query row) the chunk's max,
+// sum and unnormalised output.
+int64_t decode_workspace(const tilemix_fwd_params* p) {
+  const int64_t nchunk = ceil_div(p->max_seqlen_k, tilemix::kDecodeChunk);
+  const int64_t rmax = static_cast<int64_t>(p->hq / p->hkv) * p->max_seqlen_q;
+  return round_up(static_cast<int64_t>(p->batch) * p->hkv * nchunk * rmax * (p->head_dim + 2) * 4, 256);
+}
+
+// The kernel-side view of the shapes, inputs, route words and outputs of a call.
+tilemix::FwdArgs fwd_args(const tilemix_fwd_params* p) {
+  const float scale = p->softmax_scale > 0.0f ? p->softmax_scale
+                                              : 1.0f / std::sqrt(static_cast<float>(p->head_dim));
+  tilemix::FwdArgs a{};
+  a.hq = p->hq;
+  a.hkv = p->hkv;
+  a.total_q = p->total_q;
+  a.total_k = p->total_k;
+  a.max_seqlen_q = p->max_seqlen_q;
+  a.cu_q = p->cu_seqlens_q;
+  a.cu_k = p->cu_seqlens_k;
+  a.cu_mtiles = p->cu_mtiles;
+  a.total_mtiles = p->total_mtiles;
+  a.q = static_cast<const _Float16*>(p->q);
+  a.q_stride_tok = p->q_stride_tok;
+  a.q_stride_head = p->q_stride_head;
+  a.k = static_cast<const _Float16*>(p->k);
+  a.k_stride_tok = p->k_stride_tok;
+  a.k_stride_head = p->k_stride_head;
+  a.v = static_cast<const _Float16*>(p->v);
+  a.v_stride_tok = p->v_stride_tok;
+  a.v_stride_head = p->v_stride_head;
+  a.q8 = p->q8;
+  a.q_scale = p->q_scale;
+  a.k8 = p->k8;
+  a.k_scale = p->k_scale;
+  a.v8 = p->v8;
+  a.v_scale = p->v_scale;
+  a.words = p->route_words;
+  a.wpr = p->words_per_row;
+  a.bm_r = p->route_block_m;
+  a.bn_r = p->route_block_n;
+  a.group = p->route_group;
+  a.causal = p->causal ? 1 : 0;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out = p->out;
+  a.out_f32 = p->out_dtype == 1;
+  a.lse = p->lse;
+  a.dump = p->debug_s32;
+  a.dump_head = p->debug_head;
+  a.dump_m0 = p->debug_mtile_begin;
+  a.dump_mcount = p->debug_mtile_count;
+  a.dump_ntiles = p->debug_ntiles_max;
+  return a;
+}
+
+tilemix_status check_params(const tilemix_fwd_params* p, const char* fn) {
+  if (p == nullptr) return fail(TILEMIX_EINVAL, "%s: NULL params", fn);
+  if (p->struct_size != sizeof(tilemix_fwd_params))
+    return fail(TILEMIX_EINVAL, "%s: struct_size %u != %zu", fn, p->struct_size,
+                sizeof(tilemix_fwd_params));
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(TILEMIX_EUNSUPPORTED, "%s: head_dim %d (supported: 64, 128)", fn, p->head_dim);
+  if (p->batch < 1 || p->hq < 1 || p->hkv < 1 || p->hq % p->hkv)
+    return fail(TILEMIX_EINVAL, "%s: batch=%d hq=%d hkv=%d (need hq %% hkv == 0)", fn, p->batch,
+                p->hq, p->hkv);
+  if (p->total_q < 0 || p->total_k < 0 || p->max_seqlen_q < 0 || p->max_seqlen_k < 0 ||
+      p->total_mtiles < 0)
+    return fail(TILEMIX_EINVAL, "%s: negative size", fn);
+  if (p->route_block_m < 32 || p->route_block_m % 32)
+    return fail(TILEMIX_EINVAL, "%s: route_block_m %d is not a positive multiple of 32", fn,
+                p->route_block_m);
+  if (p->route_block_n < 64 || p->route_block_n % 64)
+    return fail(TILEMIX_EINVAL, "%s: route_block_n %d is not a positive multiple of 64", fn,
+                p->route_block_n);
+  if (p->route_group < 1) return fail(TILEMIX_EINVAL, "%s: route_group %d < 1", fn, p->route_group);
+  if (p->words_per_row < 1) return fail(TILEMIX_EINVAL, "%s: words_per_row < 1", fn);
+  const int64_t t_mask = ceil_div(p->max_seqlen_k, static_cast<int64_t>(p->route_block_n) * p->route_group);
+  if (t_mask > 64LL * p->words_per_row)
+    return fail(TILEMIX_EINVAL, "%s: %lld key-tile groups need more than %d words per row", fn,
+                (long long)t_mask, p->words_per_row);
+  if (!p->cu_seqlens_q || !p->cu_seqlens_k || !p->cu_mtiles || !p->q || !p->q8 || !p->q_scale ||
+      !p->k8 || !p->k_scale || !p->route_words || !p->out)
+    return fail(TILEMIX_EINVAL, "%s: a required pointer is NULL", fn);
+  if (p->kv_int8) {
+    if (p->k || p->v)
+      return fail(TILEMIX_EINVAL, "%s: kv_int8 takes K/V from k8/v8; k and v must be NULL", fn);
+    if (!p->v8 || !p->v_scale) return fail(TILEMIX_EINVAL, "%s: kv_int8 needs v8 and v_scale", fn);
+  } else {
+    if (!p->k || !p->v) return fail(TILEMIX_EINVAL, "%s: fp16 k and v are required", fn);
+  }
+  if (p->out_dtype != 0 && p->out_dtype != 1)
+    return fail(TILEMIX_EINVAL, "%s: out_dtype %d (0 = fp16, 1 = fp32)", fn, p->out_dtype);
+  // 16-byte vector access of the fp16 / int8 rows
+  const int64_t st[6] = {p->q_stride_tok, p->q_stride_head, p->k_stride_tok, p->k_stride_head,
+                         p->v_stride_tok, p->v_stride_head};
+  for (int i = 0; i < 6; ++i) {
+    if (i >= 2 && p->kv_int8) break;
+    if (st[i] < 0 || st[i] % 8) return fail(TILEMIX_EINVAL, "%s: fp16 strides must be multiples of 8", fn);
+  }
+  if (!aligned(p->q, 16) || (p->k && !aligned(p->k, 16)) || (p->v && !aligned(p->v, 16)) ||
+      !aligned(p->q8, 16) || !aligned(p->k8, 16) || (p->v8 && !aligned(p->v8, 16)) ||
+      !aligned(p->out, 16) || !aligned(p->k_scale, 4) || (p->v_scale && !aligned(p->v_scale, 4)))
+    return fail(TILEMIX_EINVAL, "%s: tensors must be 16-byte aligned", fn);
+  return TILEMIX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -134,53 +240,7 @@ tilemix_status tilemix_prefill_workspace_size(const tilemix_fwd_params* p, int64
 }
 
 tilemix_status tilemix_prefill_fwd(const tilemix_fwd_params* p, void* stream) {
-  if (p == nullptr) return fail(TILEMIX_EINVAL, "prefill_fwd: NULL params");
-  if (p->struct_size != sizeof(tilemix_fwd_params))
-    return fail(TILEMIX_EINVAL, "prefill_fwd: struct_size %u != %zu", p->struct_size,
-                sizeof(tilemix_fwd_params));
-  if (p->head_dim != 64 && p->head_dim != 128)
-    return fail(TILEMIX_EUNSUPPORTED, "prefill_fwd: head_dim %d (supported: 64, 128)", p->head_dim);
-  if (p->batch < 1 || p->hq < 1 || p->hkv < 1 || p->hq % p->hkv)
-    return fail(TILEMIX_EINVAL, "prefill_fwd: batch=%d hq=%d hkv=%d (need hq %% hkv == 0)", p->batch,
-                p->hq, p->hkv);
-  if (p->total_q < 0 || p->total_k < 0 || p->max_seqlen_q < 0 || p->max_seqlen_k < 0 ||
-      p->total_mtiles < 0)
-    return fail(TILEMIX_EINVAL, "prefill_fwd: negative size");
-  if (p->route_block_m < 32 || p->route_block_m % 32)
-    return fail(TILEMIX_EINVAL, "prefill_fwd: route_block_m %d is not a positive multiple of 32",
-                p->route_block_m);
-  if (p->route_block_n < 64 || p->route_block_n % 64)
-    return fail(TILEMIX_EINVAL, "prefill_fwd: route_block_n %d is not a positive multiple of 64",
-                p->route_block_n);
-  if (p->route_group < 1) return fail(TILEMIX_EINVAL, "prefill_fwd: route_group %d < 1", p->route_group);
-  if (p->words_per_row < 1) return fail(TILEMIX_EINVAL, "prefill_fwd: words_per_row < 1");
-  const int64_t t_mask = ceil_div(p->max_seqlen_k, static_cast<int64_t>(p->route_block_n) * p->route_group);
-  if (t_mask > 64LL * p->words_per_row)
-    return fail(TILEMIX_EINVAL, "prefill_fwd: %lld key-tile groups need more than %d words per row",
-                (long long)t_mask, p->words_per_row);
-  if (!p->cu_seqlens_q || !p->cu_seqlens_k || !p->cu_mtiles || !p->q || !p->q8 || !p->q_scale ||
-      !p->k8 || !p->k_scale || !p->route_words || !p->out)
-    return fail(TILEMIX_EINVAL, "prefill_fwd: a required pointer is NULL");
-  if (p->kv_int8) {
-    if (p->k || p->v)
-      return fail(TILEMIX_EINVAL, "prefill_fwd: kv_int8 takes K/V from k8/v8; k and v must be NULL");
-    if (!p->v8 || !p->v_scale) return fail(TILEMIX_EINVAL, "prefill_fwd: kv_int8 needs v8 and v_scale");
-  } else {
-    if (!p->k || !p->v) return fail(TILEMIX_EINVAL, "prefill_fwd: fp16 k and v are required");
-  }
-  if (p->out_dtype != 0 && p->out_dtype != 1)
-    return fail(TILEMIX_EINVAL, "prefill_fwd: out_dtype %d (0 = fp16, 1 = fp32)", p->out_dtype);
-  // 16-byte vector access of the fp16 / int8 rows
-  const int64_t st[6] = {p->q_stride_tok, p->q_stride_head, p->k_stride_tok, p->k_stride_head,
-                         p->v_stride_tok, p->v_stride_head};
-  for (int i = 0; i < 6; ++i) {
-    if (i >= 2 && p->kv_int8) break;
-    if (st[i] < 0 || st[i] % 8) return fail(TILEMIX_EINVAL, "prefill_fwd: fp16 strides must be multiples of 8");
-  }
-  if (!aligned(p->q, 16) || (p->k && !aligned(p->k, 16)) || (p->v && !aligned(p->v, 16)) ||
-      !aligned(p->q8, 16) || !aligned(p->k8, 16) || (p->v8 && !aligned(p->v8, 16)) ||
-      !aligned(p->out, 16) || !aligned(p->k_scale, 4) || (p->v_scale && !aligned(p->v_scale, 4)))
-    return fail(TILEMIX_EINVAL, "prefill_fwd: tensors must be 16-byte aligned");
+  if (tilemix_status st = check_params(p, "prefill_fwd")) return st;
   if (p->debug_s32) {
     if (p->debug_head < 0 || p->debug_head >= p->hq || p->debug_mtile_begin < 0 ||
         p->debug_mtile_count < 0 || p->debug_mtile_begin + p->debug_mtile_count > p->total_mtiles)
@@ -195,48 +255,7 @@ tilemix_status tilemix_prefill_fwd(const tilemix_fwd_params* p, void* stream) {
                 (long long)ws.total, (long long)p->workspace_bytes);
   if (p->total_q == 0 || p->max_seqlen_q == 0) return ok();
 
-  const float scale = p->softmax_scale > 0.0f ? p->softmax_scale
-                                              : 1.0f / std::sqrt(static_cast<float>(p->head_dim));
-  tilemix::FwdArgs a{};
-  a.hq = p->hq;
-  a.hkv = p->hkv;
-  a.total_q = p->total_q;
-  a.total_k = p->total_k;
-  a.max_seqlen_q = p->max_seqlen_q;
-  a.cu_q = p->cu_seqlens_q;
-  a.cu_k = p->cu_seqlens_k;
-  a.cu_mtiles = p->cu_mtiles;
-  a.total_mtiles = p->total_mtiles;
-  a.q = static_cast<const _Float16*>(p->q);
-  a.q_stride_tok = p->q_stride_tok;
-  a.q_stride_head = p->q_stride_head;
-  a.k = static_cast<const _Float16*>(p->k);
-  a.k_stride_tok = p->k_stride_tok;
-  a.k_stride_head = p->k_stride_head;
-  a.v = static_cast<const _Float16*>(p->v);
-  a.v_stride_tok = p->v_stride_tok;
-  a.v_stride_head = p->v_stride_head;
-  a.q8 = p->q8;
-  a.q_scale = p->q_scale;
-  a.k8 = p->k8;
-  a.k_scale = p->k_scale;
-  a.v8 = p->v8;
-  a.v_scale = p->v_scale;
-  a.words = p->route_words;
-  a.wpr = p->words_per_row;
-  a.bm_r = p->route_block_m;
-  a.bn_r = p->route_block_n;
-  a.group = p->route_group;
-  a.causal = p->causal ? 1 : 0;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  a.out = p->out;
-  a.out_f32 = p->out_dtype == 1;
-  a.lse = p->lse;
-  a.dump = p->debug_s32;
-  a.dump_head = p->debug_head;
-  a.dump_m0 = p->debug_mtile_begin;
-  a.dump_mcount = p->debug_mtile_count;
-  a.dump_ntiles = p->debug_ntiles_max;
+  tilemix::FwdArgs a = fwd_args(p);
   a.vt_ws = static_cast<_Float16*>(p->workspace);
   a.vt = a.vt_ws;
   a.vt_tiles = ws.vt_tiles;
@@ -252,6 +271,43 @@ tilemix_status tilemix_prefill_fwd(const tilemix_fwd_params* p, void* stream) {
   hipError_t e = tilemix::launch_vt_pack(a, p->batch, p->max_seqlen_k, p->head_dim, p->kv_int8 != 0, s);
   if (e != hipSuccess) return from_hip(e, "prefill_fwd (V^T pre-pass)");
   return from_hip(tilemix::launch_prefill(a, p->batch, p->head_dim, p->kv_int8 != 0, s), "prefill_fwd");
+}
+
+tilemix_status tilemix_decode_workspace_size(const tilemix_fwd_params* p, int64_t* bytes) {
+  if (p == nullptr || bytes == nullptr) return fail(TILEMIX_EINVAL, "decode_workspace_size: NULL argument");
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(TILEMIX_EUNSUPPORTED, "decode_workspace_size: head_dim %d (supported: 64, 128)", p->head_dim);
+  if (p->batch < 1 || p->hq < 1 || p->hkv < 1 || p->hq % p->hkv || p->max_seqlen_q < 0 ||
+      p->max_seqlen_k < 0)
+    return fail(TILEMIX_EINVAL, "decode_workspace_size: batch=%d hq=%d hkv=%d max_seqlen_q=%d max_seqlen_k=%d",
+                p->batch, p->hq, p->hkv, p->max_seqlen_q, p->max_seqlen_k);
+  *bytes = decode_workspace(p);
+  return ok();
+}
+
+tilemix_status tilemix_decode_fwd(const tilemix_fwd_params* p, void* stream) {
+  if (tilemix_status st = check_params(p, "decode_fwd")) return st;
+  if (!p->kv_int8)
+    return fail(TILEMIX_EUNSUPPORTED, "decode_fwd: reads an INT8 K/V cache (kv_int8 = 1)");
+  if (p->max_seqlen_q > 8)
+    return fail(TILEMIX_EUNSUPPORTED, "decode_fwd: max_seqlen_q %d > 8 (use tilemix_prefill_fwd)",
+                p->max_seqlen_q);
+  if ((p->hq / p->hkv) * p->max_seqlen_q > tilemix::kDecodeMaxRows)
+    return fail(TILEMIX_EUNSUPPORTED, "decode_fwd: (hq / hkv) * max_seqlen_q = %d > %d query rows per KV head",
+                (p->hq / p->hkv) * p->max_seqlen_q, tilemix::kDecodeMaxRows);
+  if (p->debug_s32) return fail(TILEMIX_EINVAL, "decode_fwd: the debug dump is a prefill feature");
+  const int64_t need = decode_workspace(p);
+  if (need > 0 && (p->workspace == nullptr || !aligned(p->workspace, 256) || p->workspace_bytes < need))
+    return fail(TILEMIX_EINVAL, "decode_fwd: workspace must be 256-byte aligned and hold %lld bytes (got %lld)",
+                (long long)need, (long long)p->workspace_bytes);
+  if (p->total_q == 0 || p->max_seqlen_q == 0) return ok();
+  tilemix::DecodeArgs d{};
+  d.f = fwd_args(p);
+  d.part = static_cast<float*>(p->workspace);
+  d.nchunk = static_cast<int32_t>(ceil_div(p->max_seqlen_k, tilemix::kDecodeChunk));
+  d.rmax = (p->hq / p->hkv) * p->max_seqlen_q;
+  return from_hip(tilemix::launch_decode(d, p->batch, p->head_dim, static_cast<hipStream_t>(stream)),
+                  "decode_fwd");
 }
 
 }  // extern "C"

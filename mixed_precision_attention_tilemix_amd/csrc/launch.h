@@ -60,4 +60,19 @@ hipError_t launch_vt_pack(const FwdArgs& a, int32_t batch, int32_t max_seqlen_k,
 hipError_t launch_prefill(const FwdArgs& a, int32_t batch, int32_t head_dim, bool kv_int8,
                           hipStream_t stream);
 
+// Decode over an INT8 K/V cache: keys per chunk workgroup, and the largest number of query rows
+// (query heads per KV head x query tokens) one (sequence, KV head) may carry.
+constexpr int kDecodeChunk = 256;
+constexpr int kDecodeMaxRows = 16;
+
+struct DecodeArgs {
+  FwdArgs f;          // shapes, inputs, route words and outputs (the prefill workspace fields unused)
+  float* part;        // workspace [batch][hkv][nchunk][rmax][head_dim + 2]: per chunk m, l, O
+  int32_t nchunk;     // chunks per sequence: ceil(max_seqlen_k / kDecodeChunk)
+  int32_t rmax;       // (hq / hkv) * max_seqlen_q
+};
+
+// Chunk pass then merge pass, both on `stream`.
+hipError_t launch_decode(const DecodeArgs& a, int32_t batch, int32_t head_dim, hipStream_t stream);
+
 }  // namespace tilemix

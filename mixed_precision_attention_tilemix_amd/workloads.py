@@ -24,7 +24,8 @@ from typing import List, Optional, Sequence
 
 import numpy as np
 
-__all__ = ["Workload", "make", "custom", "WORKLOADS", "varlen_lengths"]
+__all__ = ["Workload", "make", "custom", "WORKLOADS", "varlen_lengths", "DecodeWorkload",
+           "make_decode", "decode_custom", "DECODE_WORKLOADS"]
 
 
 @dataclasses.dataclass
@@ -247,3 +248,126 @@ def custom(seqlens: Sequence[int], hq: int, hk: int, d: int, *, causal: bool = T
         raise ValueError(route)
     return Workload(name, hq, hk, d, seqlens, causal, bm_r, bn_r, group, kv_int8, q, k, v, r,
                     pol, seed)
+
+
+# ----------------------------------------------------------------------------- decode
+
+@dataclasses.dataclass
+class DecodeWorkload:
+    """A few new query tokens per sequence against a cached K/V of L_k tokens (the new tokens are
+    the cache's last L_q positions, so causal alignment is bottom-right). K and V are drawn in
+    fp16; the consumer quantizes them into its INT8 cache with its own quantizer."""
+    name: str
+    hq: int
+    hk: int
+    d: int
+    q_lens: List[int]       # L_q per sequence (new tokens)
+    k_lens: List[int]       # L_k per sequence (cached tokens, the new ones included)
+    causal: bool
+    bm_r: int
+    bn_r: int
+    group: int
+    q: np.ndarray           # fp16 [sum L_q, hq, d]
+    k: np.ndarray           # fp16 [sum L_k, hk, d]
+    v: np.ndarray           # fp16 [sum L_k, hk, d]
+    route: np.ndarray       # uint8 [hk, total_mtiles, t_mask]
+    policy: str = ""
+    seed: int = 0
+    kv_int8: bool = True
+
+    @property
+    def batch(self) -> int:
+        return len(self.q_lens)
+
+    @property
+    def total_q(self) -> int:
+        return int(sum(self.q_lens))
+
+    @property
+    def total_k(self) -> int:
+        return int(sum(self.k_lens))
+
+    @property
+    def cu_q(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.q_lens)]).astype(np.int32)
+
+    @property
+    def cu_k(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.k_lens)]).astype(np.int32)
+
+    @property
+    def cu_mtiles(self) -> np.ndarray:
+        tiles = [-(-L // self.bm_r) for L in self.q_lens]
+        return np.concatenate([[0], np.cumsum(tiles)]).astype(np.int32)
+
+    @property
+    def t_mask(self) -> int:
+        return int(self.route.shape[2])
+
+    @property
+    def words_per_row(self) -> int:
+        return max(1, -(-self.t_mask // 64))
+
+    def legal_pairs(self) -> int:
+        """Legal (query, key) pairs per query head."""
+        n = 0
+        for lq, lk in zip(self.q_lens, self.k_lens):
+            for i in range(lq):
+                n += min(lk, i + lk - lq + 1) if self.causal else lk
+        return n
+
+    def describe(self) -> dict:
+        return {"workload": self.name, "batch": self.batch,
+                "q_lens": self.q_lens if self.batch <= 16 else f"{self.batch} seqs",
+                "k_lens": self.k_lens if self.batch <= 16 else f"{self.batch} seqs",
+                "hq": self.hq, "hk": self.hk, "head_dim": self.d, "causal": self.causal,
+                "route_tile": [self.bm_r, self.bn_r], "group": self.group, "t_mask": self.t_mask,
+                "kv_int8": True, "policy": self.policy, "seed": self.seed}
+
+
+def decode_custom(q_lens: Sequence[int], k_lens: Sequence[int], hq: int, hk: int, d: int, *,
+                  causal: bool = True, bm_r: int = 128, bn_r: int = 128, group: int = 1,
+                  p_fp16: float = 0.5, route: Optional[str] = None, seed: int = 0,
+                  k_std: float = 1.0, name: str = "decode") -> DecodeWorkload:
+    """Draw order: Q [sum L_q], K, V [sum L_k] (standard normal), the fp16 cast, then the route
+    map (Bernoulli p_fp16, or constant "int8" / "fp16"), one route row per query tile."""
+    rng = np.random.default_rng(seed)
+    q_lens, k_lens = [int(x) for x in q_lens], [int(x) for x in k_lens]
+    Tq, Tk = sum(q_lens), sum(k_lens)
+    q = rng.standard_normal((Tq, hq, d), dtype=np.float32)
+    k = rng.standard_normal((Tk, hk, d), dtype=np.float32) * k_std
+    v = rng.standard_normal((Tk, hk, d), dtype=np.float32)
+    q, k, v = (x.astype(np.float16) for x in (q, k, v))
+    rows = sum(-(-L // bm_r) for L in q_lens)
+    t_mask = max(1, max(-(-L // (bn_r * group)) for L in k_lens))
+    valid = []
+    for lq, lk in zip(q_lens, k_lens):
+        row = np.zeros(t_mask, dtype=bool)
+        row[:-(-lk // (bn_r * group))] = True
+        valid += [row] * (-(-lq // bm_r))
+    valid = np.stack(valid) if valid else np.zeros((0, t_mask), dtype=bool)
+    if route is None:
+        r = (rng.random((hk, rows, t_mask)) >= p_fp16).astype(np.uint8)
+        pol = f"bernoulli(p_fp16={p_fp16})"
+    else:
+        r = np.full((hk, rows, t_mask), 1 if route == "int8" else 0, dtype=np.uint8)
+        pol = "all INT8" if route == "int8" else "all FP16"
+    r &= valid[None].astype(np.uint8)
+    return DecodeWorkload(name, hq, hk, d, q_lens, k_lens, causal, bm_r, bn_r, group, q, k, v, r,
+                          pol, seed)
+
+
+def make_decode(name: str, seed: int = 0) -> DecodeWorkload:
+    """Named decode workloads: one new token against the 128k INT8 cache of the long-prefill
+    setting (32 query / 8 KV heads, route group 8, 5 % FP16 groups), and a varlen batch."""
+    if name == "decode128k":
+        return decode_custom([1], [131072], 32, 8, 128, bm_r=128, bn_r=128, group=8, p_fp16=0.05,
+                             seed=seed, name=name)
+    if name == "decode_batch":
+        return decode_custom([1, 1, 2, 4, 1, 1, 3, 1], [16384, 9000, 4096, 30000, 777, 2048, 12345, 64],
+                             32, 8, 128, bm_r=128, bn_r=128, group=2, p_fp16=0.2, seed=seed, name=name)
+    raise KeyError(name)
+
+
+DECODE_WORKLOADS = ("decode128k", "decode_batch")
+

@@ -29,9 +29,10 @@ def declared_functions():
                                  text, flags=re.M)))
 
 
-def test_header_declares_the_three_entry_points():
+def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("tilemix_quantize_qk", "tilemix_pack_route_mask", "tilemix_prefill_fwd"):
+    for n in ("tilemix_quantize_qk", "tilemix_pack_route_mask", "tilemix_prefill_fwd",
+              "tilemix_decode_fwd"):
         assert n in names
     assert set(names) == set(B.EXPORTED)
 
@@ -165,3 +166,62 @@ def test_workspace_size(lib):
 
 def test_version(lib):
     assert B.version() >= 100
+
+
+def decode_params():
+    """A valid INT8-cache decode call (GQA 4:2, one query token, 4096 cached keys)."""
+    p = base_params()
+    p.k = p.v = None
+    p.kv_int8 = 1
+    p.v8 = p.v_scale = FAKE
+    p.total_q, p.max_seqlen_q = 1, 1
+    p.total_k = p.max_seqlen_k = 4096
+    p.total_mtiles = 1
+    p.words_per_row = 1
+    return p
+
+
+DECODE_BAD_CASES = [
+    ("fp16 k/v", lambda p: (setattr(p, "kv_int8", 0), setattr(p, "k", FAKE), setattr(p, "v", FAKE)),
+     B.TILEMIX_EUNSUPPORTED),
+    ("kv_int8 with fp16 k", lambda p: setattr(p, "k", FAKE), B.TILEMIX_EINVAL),
+    ("no v8", lambda p: setattr(p, "v8", None), B.TILEMIX_EINVAL),
+    ("too many queries", lambda p: setattr(p, "max_seqlen_q", 9), B.TILEMIX_EUNSUPPORTED),
+    ("too many rows", lambda p: (setattr(p, "hq", 16), setattr(p, "hkv", 2), setattr(p, "max_seqlen_q", 4)),
+     B.TILEMIX_EUNSUPPORTED),
+    ("debug dump", lambda p: setattr(p, "debug_s32", FAKE), B.TILEMIX_EINVAL),
+    ("head_dim", lambda p: setattr(p, "head_dim", 96), B.TILEMIX_EUNSUPPORTED),
+    ("null workspace", lambda p: setattr(p, "workspace", None), B.TILEMIX_EINVAL),
+    ("small workspace", lambda p: setattr(p, "workspace_bytes", 1024), B.TILEMIX_EINVAL),
+    ("misaligned workspace", lambda p: setattr(p, "workspace", FAKE + 16), B.TILEMIX_EINVAL),
+    ("too many groups", lambda p: setattr(p, "max_seqlen_k", 128 * 65), B.TILEMIX_EINVAL),
+]
+
+
+@pytest.mark.parametrize("name,mutate,status", DECODE_BAD_CASES, ids=[c[0] for c in DECODE_BAD_CASES])
+def test_decode_validation(lib, name, mutate, status):
+    p = decode_params()
+    mutate(p)
+    got = lib.tilemix_decode_fwd(ctypes.byref(p), None)
+    assert got == status, (name, B.last_error())
+    assert B.last_error().startswith("decode_fwd")
+
+
+def test_decode_null_params(lib):
+    assert lib.tilemix_decode_fwd(None, None) == B.TILEMIX_EINVAL
+
+
+def test_decode_workspace_size(lib):
+    p = decode_params()
+    n = ctypes.c_int64(0)
+    assert lib.tilemix_decode_workspace_size(ctypes.byref(p), ctypes.byref(n)) == B.TILEMIX_OK
+    # batch x hkv x ceil(4096 / 256) chunks x (hq / hkv) * max_seqlen_q rows x (head_dim + 2) fp32
+    assert n.value == 1 * 2 * 16 * 2 * (128 + 2) * 4
+    p.max_seqlen_q = 0
+    assert lib.tilemix_decode_workspace_size(ctypes.byref(p), ctypes.byref(n)) == B.TILEMIX_OK
+    assert n.value == 0
+    p.head_dim = 80
+    assert lib.tilemix_decode_workspace_size(ctypes.byref(p), ctypes.byref(n)) == B.TILEMIX_EUNSUPPORTED
+    p.head_dim, p.hkv = 128, 3
+    assert lib.tilemix_decode_workspace_size(ctypes.byref(p), ctypes.byref(n)) == B.TILEMIX_EINVAL
+    assert lib.tilemix_decode_workspace_size(None, ctypes.byref(n)) == B.TILEMIX_EINVAL

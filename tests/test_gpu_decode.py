@@ -1,0 +1,193 @@
+"""GPU parity of tilemix_decode_fwd (a few new query tokens against an INT8 K/V cache) through the
+C ABI, against the CPU oracle's routed attention on the same quantized cache.
+
+Bars: the same as the prefill path (quantized codes bit-exact; outputs within 2e-3 max-abs with
+fp32 output, plus half an fp16 ulp with fp16 output; LSE within 1e-3), and bitwise equal runs.
+"""
+
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixed_precision_attention_tilemix_amd import binding as B
+from mixed_precision_attention_tilemix_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+LSE_TOL = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.load()
+    oracle.build()
+
+
+class DeviceDecode:
+    """A decode workload in device memory: fp16 Q, the INT8 cache quantized by the library, the
+    packed route words and the outputs."""
+
+    def __init__(self, w, out_dtype=torch.float32):
+        dev = torch.device("cuda")
+        self.w = w
+        hq, hk, d = w.hq, w.hk, w.d
+        self.q = torch.from_numpy(w.q).to(dev)
+        k = torch.from_numpy(w.k).to(dev)
+        v = torch.from_numpy(w.v).to(dev)
+        self.q8 = torch.empty((w.total_q, hq, d), dtype=torch.int8, device=dev)
+        self.q_scale = torch.empty((hq, w.total_q), dtype=torch.float32, device=dev)
+        self.k8 = torch.empty((w.total_k, hk, d), dtype=torch.int8, device=dev)
+        self.k_scale = torch.empty((hk, w.total_k), dtype=torch.float32, device=dev)
+        self.v8 = torch.empty((w.total_k, hk, d), dtype=torch.int8, device=dev)
+        self.v_scale = torch.empty((hk, w.total_k), dtype=torch.float32, device=dev)
+        if w.total_q:
+            B.tilemix_quantize_qk(q=self.q, q8=self.q8, q_scale=self.q_scale)
+        if w.total_k:
+            B.tilemix_quantize_qk(q=v, q8=self.v8, q_scale=self.v_scale, k=k, k8=self.k8,
+                                  k_scale=self.k_scale)
+        route = torch.from_numpy(np.ascontiguousarray(w.route)).to(dev)
+        self.words = torch.empty((hk, route.shape[1], w.words_per_row), dtype=torch.int64, device=dev)
+        B.tilemix_pack_route_mask(route, self.words)
+        self.cu_q = torch.from_numpy(w.cu_q).to(dev)
+        self.cu_k = torch.from_numpy(w.cu_k).to(dev)
+        self.cu_mtiles = torch.from_numpy(w.cu_mtiles).to(dev)
+        self.max_q = max(w.q_lens) if w.q_lens else 0
+        self.max_k = max(w.k_lens) if w.k_lens else 0
+        n = B.tilemix_decode_workspace_size(batch=w.batch, hq=hq, hkv=hk, head_dim=d,
+                                            max_seqlen_q=self.max_q, max_seqlen_k=self.max_k)
+        self.workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+        self.out = torch.empty((w.total_q, hq, d), dtype=out_dtype, device=dev)
+        self.lse = torch.empty((hq, w.total_q), dtype=torch.float32, device=dev)
+
+    def run(self, softmax_scale=0.0):
+        w = self.w
+        B.tilemix_decode_fwd(q=self.q, q8=self.q8, q_scale=self.q_scale, k8=self.k8,
+                             k_scale=self.k_scale, v8=self.v8, v_scale=self.v_scale,
+                             route_words=self.words, cu_seqlens_q=self.cu_q, cu_seqlens_k=self.cu_k,
+                             cu_mtiles=self.cu_mtiles, max_seqlen_q=self.max_q,
+                             max_seqlen_k=self.max_k, route_block_m=w.bm_r, route_block_n=w.bn_r,
+                             route_group=w.group, out=self.out, workspace=self.workspace,
+                             causal=w.causal, softmax_scale=softmax_scale, lse=self.lse)
+        torch.cuda.synchronize()
+        return self.out.float().cpu().numpy(), self.lse.cpu().numpy()
+
+
+def oracle_ref(w, softmax_scale=0.0):
+    q8, qs = oracle.quantize_rows(w.q)
+    k8, ks = oracle.quantize_rows(w.k)
+    v8, vs = oracle.quantize_rows(w.v)
+    p = oracle.Prepared(q=w.q, k=None, v=None, cu_q=w.cu_q, cu_k=w.cu_k, cu_mtiles=w.cu_mtiles,
+                        hq=w.hq, hk=w.hk, d=w.d, words=oracle.pack_route(w.route, w.words_per_row),
+                        bm_r=w.bm_r, bn_r=w.bn_r, group=w.group, causal=w.causal, q8=q8,
+                        q_scale=qs, k8=k8, k_scale=ks, v8=v8, v_scale=vs, kv_int8=True,
+                        softmax_scale=softmax_scale)
+    out, lse, n8, nall = p.prefill()
+    return out, lse, (q8, qs, k8, ks, v8, vs), n8, nall
+
+
+def check(out, lse, ref_out, ref_lse, what, fp16_out=False):
+    tol = TOL + (0.5 * np.spacing(np.abs(ref_out).astype(np.float16)).astype(np.float64) if fp16_out else 0.0)
+    err = np.abs(out.astype(np.float64) - ref_out.astype(np.float64))
+    assert not (err > tol).any(), f"{what}: max err {err.max():.3e} at {np.unravel_index(err.argmax(), err.shape)}"
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(np.isfinite(lse), fin), what
+    if fin.any():
+        e = np.abs(lse[fin] - ref_lse[fin]).max()
+        assert e <= LSE_TOL, f"{what}: lse err {e:.3e}"
+    return float(err.max())
+
+
+CASES = {
+    # name: (q_lens, k_lens, hq, hk, d, kwargs)
+    "gqa4_one_token": ([1], [1000], 8, 2, 128, dict(bn_r=64, group=2)),
+    "gqa4_varlen_tails": ([1, 3, 2], [4097, 255, 64], 8, 2, 128, dict(bn_r=64, group=1)),
+    "mha_eight_tokens": ([8, 5], [700, 300], 2, 2, 128, dict(bn_r=128, group=1)),
+    "gqa8_two_tokens_max_rows": ([2], [2000], 16, 2, 128, dict(bn_r=64, group=3)),
+    "d64": ([1, 2], [513, 1500], 4, 2, 64, dict(bn_r=64, group=2)),
+    "all_int8": ([1, 4], [3000, 1024], 8, 2, 128, dict(route="int8")),
+    "all_fp16": ([1, 4], [3000, 1024], 8, 2, 128, dict(route="fp16")),
+    "non_causal": ([3], [999], 4, 1, 128, dict(causal=False, bn_r=64)),
+    "fewer_keys_than_queries": ([6], [3], 4, 2, 128, dict(bn_r=64)),
+    "single_key": ([1], [1], 4, 4, 128, dict()),
+    "large_keys": ([1], [2500], 4, 2, 128, dict(k_std=8.0, bn_r=64)),
+}
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_decode_parity(case):
+    q_lens, k_lens, hq, hk, d, kw = CASES[case]
+    w = wl.decode_custom(q_lens, k_lens, hq, hk, d, seed=11, name=case, **kw)
+    dev = DeviceDecode(w)
+    out, lse = dev.run()
+    ref_out, ref_lse, (q8, qs, k8, ks, v8, vs), n8, nall = oracle_ref(w)
+    # the library's quantizer produced the oracle's cache bit for bit
+    assert np.array_equal(dev.k8.cpu().numpy(), k8) and np.array_equal(dev.v8.cpu().numpy(), v8)
+    assert np.array_equal(dev.v_scale.cpu().numpy().view(np.uint32), vs.T.view(np.uint32))
+    assert np.array_equal(dev.q8.cpu().numpy(), q8)
+    check(out, lse, ref_out, ref_lse, case)
+    if case == "fewer_keys_than_queries":
+        # bottom-right alignment: queries 0..2 of 6 see no key
+        assert np.all(out[:3] == 0) and np.all(np.isneginf(lse[:, :3]))
+
+
+def test_decode_fp16_output_and_scale():
+    w = wl.decode_custom([2, 1], [1500, 333], 8, 2, 128, bn_r=64, group=2, seed=3)
+    dev = DeviceDecode(w, out_dtype=torch.float16)
+    out, lse = dev.run(softmax_scale=0.05)
+    ref_out, ref_lse, *_ = oracle_ref(w, softmax_scale=0.05)
+    check(out, lse, ref_out, ref_lse, "fp16 out, scale 0.05", fp16_out=True)
+
+
+def test_decode_deterministic_and_matches_prefill_path():
+    w = wl.decode_custom([1, 4, 2], [2049, 700, 64], 8, 2, 128, bn_r=64, group=2, seed=9)
+    dev = DeviceDecode(w)
+    o1, l1 = dev.run()
+    o1, l1 = o1.copy(), l1.copy()
+    o2, l2 = dev.run()
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+    assert np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
+    # the prefill kernel on the same cache (fp16-rounded P there, fp32 P here)
+    out_p = torch.empty_like(dev.out)
+    lse_p = torch.empty_like(dev.lse)
+    n = B.tilemix_prefill_workspace_size(batch=w.batch, hkv=w.hk, head_dim=w.d, total_k=w.total_k,
+                                         kv_int8=True)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    B.tilemix_prefill_fwd(q=dev.q, q8=dev.q8, q_scale=dev.q_scale, k8=dev.k8, k_scale=dev.k_scale,
+                          v8=dev.v8, v_scale=dev.v_scale, route_words=dev.words,
+                          cu_seqlens_q=dev.cu_q, cu_seqlens_k=dev.cu_k, cu_mtiles=dev.cu_mtiles,
+                          max_seqlen_q=dev.max_q, max_seqlen_k=dev.max_k, route_block_m=w.bm_r,
+                          route_block_n=w.bn_r, route_group=w.group, out=out_p, workspace=ws,
+                          causal=True, lse=lse_p)
+    torch.cuda.synchronize()
+    assert np.abs(out_p.cpu().numpy() - o1).max() <= 2 * TOL
+    assert np.abs(lse_p.cpu().numpy() - l1).max() <= LSE_TOL
+
+
+def test_decode_empty_cache_and_no_queries():
+    # a sequence with no cached key: O = 0, LSE = -inf; a sequence with no new token: untouched
+    w = wl.decode_custom([1, 2, 0], [0, 300, 50], 4, 2, 128, bn_r=64, seed=4)
+    dev = DeviceDecode(w)
+    out, lse = dev.run()
+    ref_out, ref_lse, *_ = oracle_ref(w)
+    check(out, lse, ref_out, ref_lse, "empty cache")
+    assert np.all(out[0] == 0) and np.all(np.isneginf(lse[:, 0]))
+
+
+@functools.lru_cache(maxsize=None)
+def named(name):
+    return wl.make_decode(name)
+
+
+@pytest.mark.parametrize("name", wl.DECODE_WORKLOADS)
+def test_decode_named_workloads(name):
+    w = named(name)
+    dev = DeviceDecode(w, out_dtype=torch.float16)
+    out, lse = dev.run()
+    ref_out, ref_lse, *_ = oracle_ref(w)
+    check(out, lse, ref_out, ref_lse, name, fp16_out=True)
