@@ -114,6 +114,104 @@ def cpu_baseline(w, prob, rows):
     }
 
 
+def decode_bytes(w):
+    """Algorithmic HBM bytes of one tilemix_decode_fwd call: every cached key / value row a query
+    can see, read once per KV head (int8 K and V rows + their two fp32 scales), the new tokens'
+    fp16 and int8 query rows + scale, and the fp16 outputs + LSE."""
+    kv = 0
+    for lq, lk in zip(w.q_lens, w.k_lens):
+        if lq:
+            kv += lk * w.hk * (2 * w.d + 8)
+    q = w.total_q * w.hq * (3 * w.d + 4)
+    out = w.total_q * w.hq * (2 * w.d + 4)
+    return kv + q + out
+
+
+def run_decode(args):
+    """One step = tilemix_quantize_qk on the new tokens + tilemix_decode_fwd against the cache."""
+    import torch
+    from mixed_precision_attention_tilemix_amd import binding, workloads
+    from mixed_precision_attention_tilemix_amd.runner import DeviceDecode
+
+    binding.load()
+    w = workloads.make_decode(args.workload)
+    prob = DeviceDecode(w, out_dtype=torch.float16)
+    stream = torch.cuda.current_stream()
+    nbytes = decode_bytes(w)
+    for _ in range(args.warmup):
+        prob.step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1, e2 in ev:
+        e0.record(stream)
+        prob.quantize()
+        e1.record(stream)
+        prob.decode()
+        e2.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_ms = float(np.mean([e1.elapsed_time(e2) for _, e1, e2 in ev]))
+    q_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1, _ in ev]))
+    step_ms = wall * 1e3 / args.steps
+    gbps = nbytes / (step_ms * 1e-3) / 1e9
+    dec_gbps = nbytes / (dec_ms * 1e-3) / 1e9
+    result = {
+        "metric": "routed decode over the INT8 K/V cache: effective HBM bandwidth",
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 K/V, fp32 softmax and P.V",
+        "data": "synthetic",
+        "config": dict(w.describe(), out_dtype="fp16"),
+        "tokens_per_s": round(w.total_q / (step_ms * 1e-3), 1),
+        "decode_ms": round(dec_ms, 4),
+        "quantize_q_ms": round(q_ms, 4),
+        "roofline": {
+            "kernel": "decode_chunk_kernel<128> + decode_merge_kernel<128> (the tilemix_decode_fwd call)",
+            "bound": "hbm",
+            "achieved": round(dec_gbps, 1),
+            "peak": PEAK_HBM,
+            "unit": "GB/s",
+            "frac": round(dec_gbps / PEAK_HBM, 4),
+            "traffic": None,
+            "bytes_per_launch": nbytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        q8, qs = oracle.quantize_rows(w.q)
+        k8, ks = oracle.quantize_rows(w.k)
+        v8, vs = oracle.quantize_rows(w.v)
+        prep = oracle.Prepared(q=w.q, k=None, v=None, cu_q=w.cu_q, cu_k=w.cu_k, cu_mtiles=w.cu_mtiles,
+                               hq=w.hq, hk=w.hk, d=w.d, words=oracle.pack_route(w.route, w.words_per_row),
+                               bm_r=w.bm_r, bn_r=w.bn_r, group=w.group, causal=w.causal, q8=q8,
+                               q_scale=qs, k8=k8, k_scale=ks, v8=v8, v_scale=vs, kv_int8=True)
+        t1 = time.perf_counter()
+        ref, _, _, nall = prep.prefill()
+        dt = time.perf_counter() - t1
+        gpu = prob.out.float().cpu().numpy()
+        result["cpu_baseline"] = {
+            "value": round(nbytes / dt / 1e9, 3),
+            "unit": "GB/s",
+            "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"the whole step ({w.total_q} new tokens x {w.hq} heads, {nall} legal pairs), "
+                      f"fp64 oracle, {dt:.2f} s",
+            "seconds": dt,
+            "parity_max_abs_err": float(np.abs(gpu.astype(np.float64) - ref).max()),
+        }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -126,6 +224,11 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards by KV head with no exchange; see the design notes)", file=sys.stderr)
         sys.exit(2)
+
+    from mixed_precision_attention_tilemix_amd import workloads as _wl
+    if args.workload in _wl.DECODE_WORKLOADS:
+        run_decode(args)
+        return
 
     import torch
     from mixed_precision_attention_tilemix_amd import binding, workloads

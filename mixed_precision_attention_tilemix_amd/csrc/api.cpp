@@ -79,7 +79,7 @@ WorkspaceLayout workspace_layout(const tilemix_fwd_params* p) {
 int64_t decode_workspace(const tilemix_fwd_params* p) {
   const int64_t nchunk = ceil_div(p->max_seqlen_k, tilemix::kDecodeChunk);
   const int64_t rmax = static_cast<int64_t>(p->hq / p->hkv) * p->max_seqlen_q;
-  return round_up(static_cast<int64_t>(p->batch) * p->hkv * nchunk * rmax * (p->head_dim + 2) * 4, 256);
+  return round_up(static_cast<int64_t>(p->batch) * p->hkv * nchunk * rmax * (p->head_dim + 4) * 4, 256);
 }
 
 // The kernel-side view of the shapes, inputs, route words and outputs of a call.

@@ -62,12 +62,12 @@ hipError_t launch_prefill(const FwdArgs& a, int32_t batch, int32_t head_dim, boo
 
 // Decode over an INT8 K/V cache: keys per chunk workgroup, and the largest number of query rows
 // (query heads per KV head x query tokens) one (sequence, KV head) may carry.
-constexpr int kDecodeChunk = 256;
+constexpr int kDecodeChunk = 1024;
 constexpr int kDecodeMaxRows = 16;
 
 struct DecodeArgs {
   FwdArgs f;          // shapes, inputs, route words and outputs (the prefill workspace fields unused)
-  float* part;        // workspace [batch][hkv][nchunk][rmax][head_dim + 2]: per chunk m, l, O
+  float* part;        // workspace [batch][hkv][nchunk][rmax][head_dim + 4]: per chunk m, l, 2 pad, O
   int32_t nchunk;     // chunks per sequence: ceil(max_seqlen_k / kDecodeChunk)
   int32_t rmax;       // (hq / hkv) * max_seqlen_q
 };

@@ -83,3 +83,62 @@ class DeviceProblem:
         self.quantize(stream)
         self.pack(stream)
         self.attention(stream)
+
+
+class DeviceDecode:
+    """A decode workload in device memory: fp16 Q of the new tokens, the INT8 K/V cache
+    (quantized once at construction by the library's own quantizer; the fp16 K/V are dropped),
+    the packed route words and the outputs.
+
+    ``step()`` is one decode step: tilemix_quantize_qk on the new query tokens, then
+    tilemix_decode_fwd against the cache, both on the current stream."""
+
+    def __init__(self, w, device: str = "cuda", out_dtype=torch.float16, with_lse: bool = True):
+        dev = torch.device(device)
+        self.w = w
+        hq, hk, d = w.hq, w.hk, w.d
+        self.q = torch.from_numpy(w.q).to(dev)
+        self.q8 = torch.empty((w.total_q, hq, d), dtype=torch.int8, device=dev)
+        self.q_scale = torch.empty((hq, w.total_q), dtype=torch.float32, device=dev)
+        self.k8 = torch.empty((w.total_k, hk, d), dtype=torch.int8, device=dev)
+        self.k_scale = torch.empty((hk, w.total_k), dtype=torch.float32, device=dev)
+        self.v8 = torch.empty((w.total_k, hk, d), dtype=torch.int8, device=dev)
+        self.v_scale = torch.empty((hk, w.total_k), dtype=torch.float32, device=dev)
+        if w.total_k:
+            k = torch.from_numpy(w.k).to(dev)
+            v = torch.from_numpy(w.v).to(dev)
+            B.tilemix_quantize_qk(q=v, q8=self.v8, q_scale=self.v_scale, k=k, k8=self.k8,
+                                  k_scale=self.k_scale)
+            del k, v
+        route = torch.from_numpy(np.ascontiguousarray(w.route)).to(dev)
+        self.words = torch.empty((hk, route.shape[1], w.words_per_row), dtype=torch.int64, device=dev)
+        B.tilemix_pack_route_mask(route, self.words)
+        self.cu_q = torch.from_numpy(w.cu_q).to(dev)
+        self.cu_k = torch.from_numpy(w.cu_k).to(dev)
+        self.cu_mtiles = torch.from_numpy(w.cu_mtiles).to(dev)
+        self.max_q = max(w.q_lens) if w.q_lens else 0
+        self.max_k = max(w.k_lens) if w.k_lens else 0
+        n = B.tilemix_decode_workspace_size(batch=w.batch, hq=hq, hkv=hk, head_dim=d,
+                                            max_seqlen_q=self.max_q, max_seqlen_k=self.max_k)
+        self.workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+        self.out = torch.empty((w.total_q, hq, d), dtype=out_dtype, device=dev)
+        self.lse = torch.empty((hq, w.total_q), dtype=torch.float32, device=dev) if with_lse else None
+
+    def quantize(self, stream=None):
+        if self.w.total_q:
+            B.tilemix_quantize_qk(q=self.q, q8=self.q8, q_scale=self.q_scale, stream=stream)
+
+    def decode(self, softmax_scale: float = 0.0, stream=None):
+        w = self.w
+        B.tilemix_decode_fwd(q=self.q, q8=self.q8, q_scale=self.q_scale, k8=self.k8,
+                             k_scale=self.k_scale, v8=self.v8, v_scale=self.v_scale,
+                             route_words=self.words, cu_seqlens_q=self.cu_q, cu_seqlens_k=self.cu_k,
+                             cu_mtiles=self.cu_mtiles, max_seqlen_q=self.max_q,
+                             max_seqlen_k=self.max_k, route_block_m=w.bm_r, route_block_n=w.bn_r,
+                             route_group=w.group, out=self.out, workspace=self.workspace,
+                             causal=w.causal, softmax_scale=softmax_scale, lse=self.lse,
+                             stream=stream)
+
+    def step(self, stream=None):
+        self.quantize(stream)
+        self.decode(stream=stream)

@@ -215,8 +215,8 @@ def test_decode_workspace_size(lib):
     p = decode_params()
     n = ctypes.c_int64(0)
     assert lib.tilemix_decode_workspace_size(ctypes.byref(p), ctypes.byref(n)) == B.TILEMIX_OK
-    # batch x hkv x ceil(4096 / 256) chunks x (hq / hkv) * max_seqlen_q rows x (head_dim + 2) fp32
-    assert n.value == 1 * 2 * 16 * 2 * (128 + 2) * 4
+    # batch x hkv x ceil(4096 / 1024) chunks x (hq / hkv) * max_seqlen_q rows x (head_dim + 4) fp32
+    assert n.value == 1 * 2 * 4 * 2 * (128 + 4) * 4
     p.max_seqlen_q = 0
     assert lib.tilemix_decode_workspace_size(ctypes.byref(p), ctypes.byref(n)) == B.TILEMIX_OK
     assert n.value == 0

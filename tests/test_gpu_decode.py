@@ -13,6 +13,7 @@ import torch
 
 import oracle
 from mixed_precision_attention_tilemix_amd import binding as B
+from mixed_precision_attention_tilemix_amd import runner
 from mixed_precision_attention_tilemix_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -29,51 +30,15 @@ def gpu_ready():
     oracle.build()
 
 
-class DeviceDecode:
-    """A decode workload in device memory: fp16 Q, the INT8 cache quantized by the library, the
-    packed route words and the outputs."""
+class DeviceDecode(runner.DeviceDecode):
+    """The package's device-side decode problem, quantizing the new tokens at construction."""
 
     def __init__(self, w, out_dtype=torch.float32):
-        dev = torch.device("cuda")
-        self.w = w
-        hq, hk, d = w.hq, w.hk, w.d
-        self.q = torch.from_numpy(w.q).to(dev)
-        k = torch.from_numpy(w.k).to(dev)
-        v = torch.from_numpy(w.v).to(dev)
-        self.q8 = torch.empty((w.total_q, hq, d), dtype=torch.int8, device=dev)
-        self.q_scale = torch.empty((hq, w.total_q), dtype=torch.float32, device=dev)
-        self.k8 = torch.empty((w.total_k, hk, d), dtype=torch.int8, device=dev)
-        self.k_scale = torch.empty((hk, w.total_k), dtype=torch.float32, device=dev)
-        self.v8 = torch.empty((w.total_k, hk, d), dtype=torch.int8, device=dev)
-        self.v_scale = torch.empty((hk, w.total_k), dtype=torch.float32, device=dev)
-        if w.total_q:
-            B.tilemix_quantize_qk(q=self.q, q8=self.q8, q_scale=self.q_scale)
-        if w.total_k:
-            B.tilemix_quantize_qk(q=v, q8=self.v8, q_scale=self.v_scale, k=k, k8=self.k8,
-                                  k_scale=self.k_scale)
-        route = torch.from_numpy(np.ascontiguousarray(w.route)).to(dev)
-        self.words = torch.empty((hk, route.shape[1], w.words_per_row), dtype=torch.int64, device=dev)
-        B.tilemix_pack_route_mask(route, self.words)
-        self.cu_q = torch.from_numpy(w.cu_q).to(dev)
-        self.cu_k = torch.from_numpy(w.cu_k).to(dev)
-        self.cu_mtiles = torch.from_numpy(w.cu_mtiles).to(dev)
-        self.max_q = max(w.q_lens) if w.q_lens else 0
-        self.max_k = max(w.k_lens) if w.k_lens else 0
-        n = B.tilemix_decode_workspace_size(batch=w.batch, hq=hq, hkv=hk, head_dim=d,
-                                            max_seqlen_q=self.max_q, max_seqlen_k=self.max_k)
-        self.workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
-        self.out = torch.empty((w.total_q, hq, d), dtype=out_dtype, device=dev)
-        self.lse = torch.empty((hq, w.total_q), dtype=torch.float32, device=dev)
+        super().__init__(w, out_dtype=out_dtype)
+        self.quantize()
 
     def run(self, softmax_scale=0.0):
-        w = self.w
-        B.tilemix_decode_fwd(q=self.q, q8=self.q8, q_scale=self.q_scale, k8=self.k8,
-                             k_scale=self.k_scale, v8=self.v8, v_scale=self.v_scale,
-                             route_words=self.words, cu_seqlens_q=self.cu_q, cu_seqlens_k=self.cu_k,
-                             cu_mtiles=self.cu_mtiles, max_seqlen_q=self.max_q,
-                             max_seqlen_k=self.max_k, route_block_m=w.bm_r, route_block_n=w.bn_r,
-                             route_group=w.group, out=self.out, workspace=self.workspace,
-                             causal=w.causal, softmax_scale=softmax_scale, lse=self.lse)
+        self.decode(softmax_scale=softmax_scale)
         torch.cuda.synchronize()
         return self.out.float().cpu().numpy(), self.lse.cpu().numpy()
 
