@@ -33,6 +33,8 @@ WORKLOAD = "gqa32k"
 CAL_BYTES = 256 << 20   # plain device copy of known size: calibrates the HBM byte counters
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_fwd_gqa32k_traffic.md")
 KERNEL_SRC = os.path.join(ROOT, "mixed_precision_attention_tilemix_amd", "csrc", "prefill_fwd.hip")
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_fwd_decode128k.md")
+DECODE_SRC = os.path.join(ROOT, "mixed_precision_attention_tilemix_amd", "csrc", "decode.hip")
 
 
 def calibration_copy():
@@ -47,15 +49,15 @@ def calibration_copy():
     del src, dst
 
 
-def measured_traffic():
-    """HBM bytes per fused-kernel launch from the committed counter summary, or None when the
-    summary is missing or was taken on a different kernel source."""
+def measured_traffic(traffic_file=TRAFFIC_FILE, kernel_src=KERNEL_SRC):
+    """HBM bytes per launch from a committed counter summary, or None when the summary is
+    missing or was taken on a different kernel source."""
     import hashlib
-    if not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(traffic_file):
         return None
-    digest = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    digest = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
     fields = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(traffic_file):
         if ":" in line and line.strip().startswith("- "):
             k, v = line.strip()[2:].split(":", 1)
             fields[k.strip()] = v.strip().strip("`")
@@ -182,7 +184,7 @@ def run_decode(args):
             "peak": PEAK_HBM,
             "unit": "GB/s",
             "frac": round(dec_gbps / PEAK_HBM, 4),
-            "traffic": None,
+            "traffic": measured_traffic(DECODE_TRAFFIC_FILE, DECODE_SRC) if w.name == "decode128k" else None,
             "bytes_per_launch": nbytes,
         },
     }
