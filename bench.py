@@ -214,6 +214,72 @@ def run_decode(args):
     print(json.dumps(result), flush=True)
 
 
+def exact_attention_cpu(w):
+    """Causal softmax attention of the fp16 inputs in fp64 with plain PyTorch CPU ops: the
+    reference of the deviation sweep (independent of the routed kernel and of the oracle)."""
+    import torch
+    L, d = w.total, w.d
+    q = torch.from_numpy(w.q.astype(np.float64))
+    k = torch.from_numpy(w.k.astype(np.float64))
+    v = torch.from_numpy(w.v.astype(np.float64))
+    out = torch.empty((L, w.hq, d), dtype=torch.float64)
+    grp = w.hq // w.hk
+    mask = torch.ones((L, L), dtype=torch.bool).tril()
+    for h in range(w.hq):
+        s = (q[:, h] @ k[:, h // grp].T) / np.sqrt(d)
+        s.masked_fill_(~mask, float("-inf"))
+        out[:, h] = torch.softmax(s, dim=-1) @ v[:, h // grp]
+    return out.numpy()
+
+
+def run_numerics(args):
+    """Mean absolute output deviation of the routed kernel from exact attention, by sequence length
+    and INT8 tile-group coverage (the paper's Table 3 study) on randomized inputs."""
+    import torch
+    from mixed_precision_attention_tilemix_amd import binding, workloads
+    from mixed_precision_attention_tilemix_amd.runner import DeviceProblem
+
+    binding.load()
+    table = {}
+    t0 = time.perf_counter()
+    for L in workloads.NUMERICS_LENGTHS:
+        exact = None
+        row = {}
+        for cov in workloads.NUMERICS_COVERAGES:
+            w = workloads.numerics_case(L, cov)
+            if exact is None:
+                exact = exact_attention_cpu(w)
+            prob = DeviceProblem(w, out_dtype=torch.float32)
+            prob.step()
+            torch.cuda.synchronize()
+            out = prob.out.cpu().numpy().astype(np.float64)
+            n8 = int8_pair_counts(w)
+            row[f"{int(round(100 * cov))}%"] = {
+                "mean_abs_dev": float(np.abs(out - exact).mean()),
+                "max_abs_dev": float(np.abs(out - exact).max()),
+                "int8_pair_fraction": round(n8 / (w.legal_pairs() * w.hq), 4),
+            }
+            del prob
+        table[str(L)] = row
+    last = table[str(workloads.NUMERICS_LENGTHS[-1])][f"{int(round(100 * workloads.NUMERICS_COVERAGES[-1]))}%"]
+    result = {
+        "metric": "mean |O - O_exact| of routed prefill by INT8 tile-group coverage (randomized inputs)",
+        "value": last["mean_abs_dev"],
+        "unit": "abs",
+        "n_gpus": 1,
+        "higher_is_better": False,
+        "data": "synthetic",
+        "dtype": "fp16+int8 (fp32 accumulate), fp32 output",
+        "config": {"workload": "numerics", "hq": 24, "hkv": 8, "head_dim": 128, "causal": True,
+                   "route_tile": [64, 64], "group": 1, "lengths": list(workloads.NUMERICS_LENGTHS),
+                   "int8_coverages": list(workloads.NUMERICS_COVERAGES),
+                   "reference": "exact causal attention of the fp16 inputs, fp64, PyTorch CPU"},
+        "table": table,
+        "seconds": round(time.perf_counter() - t0, 1),
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -228,6 +294,9 @@ def main():
         sys.exit(2)
 
     from mixed_precision_attention_tilemix_amd import workloads as _wl
+    if args.workload == "numerics":
+        run_numerics(args)
+        return
     if args.workload in _wl.DECODE_WORKLOADS:
         run_decode(args)
         return

@@ -25,7 +25,8 @@ from typing import List, Optional, Sequence
 import numpy as np
 
 __all__ = ["Workload", "make", "custom", "WORKLOADS", "varlen_lengths", "DecodeWorkload",
-           "make_decode", "decode_custom", "DECODE_WORKLOADS"]
+           "make_decode", "decode_custom", "DECODE_WORKLOADS", "numerics_case", "NUMERICS_LENGTHS",
+           "NUMERICS_COVERAGES"]
 
 
 @dataclasses.dataclass
@@ -249,6 +250,29 @@ def custom(seqlens: Sequence[int], hq: int, hk: int, d: int, *, causal: bool = T
     return Workload(name, hq, hk, d, seqlens, causal, bm_r, bn_r, group, kv_int8, q, k, v, r,
                     pol, seed)
 
+
+
+# ----------------------------------------------------------------------------- numerics sweep
+
+NUMERICS_LENGTHS = (1024, 2048, 4096, 8192)
+NUMERICS_COVERAGES = (0.0, 0.05, 0.10, 0.15, 0.20, 0.25)
+
+
+def numerics_case(L: int, int8_coverage: float, seed: int = 0) -> Workload:
+    """Randomized attention inputs for the output-deviation sweep over INT8 tile-group coverage
+    (the setting of the TileMix paper's Section 5.4 / Table 3): one causal sequence of L tokens,
+    24 query / 8 KV heads of 128 channels (the head layout of the 3B model the paper times),
+    64 x 64 route tiles, one tile per routing bit, each group INT8 with probability
+    int8_coverage. Inputs do not depend on the coverage, only the route map does."""
+    rng = np.random.default_rng(seed)
+    hq, hk, d, bm_r, bn_r, g = 24, 8, 128, 64, 64, 1
+    q, k, v = _draw_qkv(rng, L, hq, hk, d)
+    q, k, v = (x.astype(np.float16) for x in (q, k, v))
+    rrng = np.random.default_rng([seed, int(round(int8_coverage * 10000))])
+    route = route_bernoulli(rrng, hk, [L], bm_r, bn_r, g, 1.0 - int8_coverage)
+    return Workload(f"numerics_L{L}_int8_{int(round(100 * int8_coverage))}pct", hq, hk, d, [L], True,
+                    bm_r, bn_r, g, False, q, k, v, route,
+                    f"bernoulli(int8_coverage={int8_coverage})", seed)
 
 # ----------------------------------------------------------------------------- decode
 
