@@ -67,6 +67,15 @@ def lib():
                                      ctypes.c_void_p]
         L.oracle_int32_tiles.argtypes = [ctypes.POINTER(Problem), ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+        L.oracle_philox4x32_10.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.oracle_philox4x32_10.restype = None
+        L.oracle_route_topk_maxabs.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+        L.oracle_route_bernoulli.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_uint64, ctypes.c_int32, ctypes.c_void_p]
         L.oracle_decode_fp16.argtypes = [ctypes.c_uint16]
         L.oracle_decode_fp16.restype = ctypes.c_double
         _lib = L
@@ -109,6 +118,52 @@ def pack_route(route: np.ndarray, wpr: Optional[int] = None) -> np.ndarray:
     if rc:
         raise ValueError("oracle_pack_route rejected its arguments")
     return words
+
+
+def philox4x32_10(ctr, key) -> np.ndarray:
+    """Philox4x32-10 of a 4-word counter and a 2-word key -> 4 uint32 words."""
+    c = np.asarray(ctr, dtype=np.uint32).copy()
+    k = np.asarray(key, dtype=np.uint32).copy()
+    out = np.empty(4, dtype=np.uint32)
+    lib().oracle_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def _route_geometry(cu_k, cu_mtiles, bn_r, group, t_mask):
+    cu_k = np.ascontiguousarray(cu_k, dtype=np.int32)
+    cu_mtiles = np.ascontiguousarray(cu_mtiles, dtype=np.int32)
+    span = bn_r * group
+    if t_mask is None:
+        t_mask = max(1, int(max(-(-int(n) // span) for n in np.diff(cu_k))))
+    return cu_k, cu_mtiles, int(t_mask)
+
+
+def route_topk_maxabs(cu_k, cu_mtiles, hk, d, bn_r, group, per_mille, *, k=None, k8=None,
+                      k_scale=None, t_mask=None) -> np.ndarray:
+    """Top-k by max|K| routing map R [hk, total_mtiles, t_mask] (uint8, 1 = INT8).
+
+    k: fp16 [total_k, hk, d]; or k8 int8 [total_k, hk, d] with k_scale fp32 [total_k, hk]."""
+    cu_k, cu_mtiles, t_mask = _route_geometry(cu_k, cu_mtiles, bn_r, group, t_mask)
+    kb = None if k is None else np.ascontiguousarray(k, dtype=np.float16).view(np.uint16)
+    k8 = None if k8 is None else np.ascontiguousarray(k8, dtype=np.int8)
+    ks = None if k_scale is None else np.ascontiguousarray(k_scale, dtype=np.float32)
+    R = np.empty((hk, int(cu_mtiles[-1]), t_mask), dtype=np.uint8)
+    rc = lib().oracle_route_topk_maxabs(_ptr(cu_k), _ptr(cu_mtiles), len(cu_k) - 1, hk, d, _ptr(kb),
+                                        _ptr(k8), _ptr(ks), bn_r, group, per_mille, t_mask, _ptr(R))
+    if rc:
+        raise ValueError("oracle_route_topk_maxabs rejected its arguments")
+    return R
+
+
+def route_bernoulli(cu_k, cu_mtiles, hk, bn_r, group, per_mille, seed, *, t_mask=None) -> np.ndarray:
+    """Coverage-budget Bernoulli routing map R [hk, total_mtiles, t_mask] (uint8, 1 = INT8)."""
+    cu_k, cu_mtiles, t_mask = _route_geometry(cu_k, cu_mtiles, bn_r, group, t_mask)
+    R = np.empty((hk, int(cu_mtiles[-1]), t_mask), dtype=np.uint8)
+    rc = lib().oracle_route_bernoulli(_ptr(cu_k), _ptr(cu_mtiles), len(cu_k) - 1, hk, bn_r, group,
+                                      per_mille, int(seed), t_mask, _ptr(R))
+    if rc:
+        raise ValueError("oracle_route_bernoulli rejected its arguments")
+    return R
 
 
 class Prepared:

@@ -372,3 +372,145 @@ int oracle_int32_tiles(const oracle_problem* prob, int32_t head, int32_t m0, int
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------------------------
+// Routing policies: the step that produces R before packing. The pages let any static or adaptive
+// policy supply R (TileMix paper, Section 4.2 "Policy definition", and the Limitations section);
+// their own templates are defined in an appendix the pages do not hold. These are the two policies
+// the library computes on the device (readings listed with the others in the design notes):
+//   * top-k by max|K|: per sequence and KV head, the ceil(T * per_mille / 1000) key-tile groups
+//     with the largest max|K| over their keys and channels take the FP16 path (R = 0) in every
+//     query-tile row of the sequence; ties go to the lower group index; the other groups below the
+//     sequence's T = ceil(L_k / (BN_r * g)) are INT8 (R = 1). With an INT8 cache, |K| of a key is
+//     the fp32 product k_scale * |k8|.
+//   * coverage-budget Bernoulli: every (KV head, route row, group) below T is FP16 iff the first
+//     output word of Philox4x32-10 at counter (g_j, route row, h_k, 0) and key (seed low 32 bits,
+//     seed high 32 bits) is below thr = floor(per_mille * 2^32 / 1000).
+// R is [hk, total_mtiles, t_mask]; groups at or past a sequence's own T are 0.
+
+namespace {
+
+// One Philox4x32 round and the Weyl key schedule, from the generator's definition in Salmon,
+// Moraes, Dror and Shaw, "Parallel random numbers: as easy as 1, 2, 3" (SC 2011).
+void philox_round(uint32_t x[4], const uint32_t k[2]) {
+  const uint64_t p0 = static_cast<uint64_t>(0xD2511F53u) * x[0];
+  const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * x[2];
+  const uint32_t hi0 = static_cast<uint32_t>(p0 >> 32), lo0 = static_cast<uint32_t>(p0);
+  const uint32_t hi1 = static_cast<uint32_t>(p1 >> 32), lo1 = static_cast<uint32_t>(p1);
+  const uint32_t y0 = hi1 ^ x[1] ^ k[0];
+  const uint32_t y2 = hi0 ^ x[3] ^ k[1];
+  x[0] = y0;
+  x[1] = lo1;
+  x[2] = y2;
+  x[3] = lo0;
+}
+
+void philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  uint32_t x[4] = {ctr[0], ctr[1], ctr[2], ctr[3]};
+  uint32_t k[2] = {key[0], key[1]};
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) {
+      k[0] += 0x9E3779B9u;
+      k[1] += 0xBB67AE85u;
+    }
+    philox_round(x, k);
+  }
+  for (int i = 0; i < 4; ++i) out[i] = x[i];
+}
+
+// Shared argument checks of the two policies; on success *span is BN_r * g.
+int check_route_args(const int32_t* cu_k, const int32_t* cu_mtiles, int32_t batch, int32_t hk,
+                     int32_t bn_r, int32_t group, int32_t per_mille, int32_t t_mask, uint8_t* R,
+                     int64_t* span) {
+  if (!cu_k || !cu_mtiles || !R || batch < 1 || hk < 1 || bn_r < 1 || group < 1 || t_mask < 0 ||
+      per_mille < 0 || per_mille > 1000)
+    return -1;
+  *span = static_cast<int64_t>(bn_r) * group;
+  for (int b = 0; b < batch; ++b) {
+    const int64_t Lk = cu_k[b + 1] - cu_k[b];
+    if (Lk < 0 || cu_mtiles[b + 1] < cu_mtiles[b]) return -1;
+    if ((Lk + *span - 1) / *span > t_mask) return -1;
+  }
+  return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+void oracle_philox4x32_10(const uint32_t* ctr, const uint32_t* key, uint32_t* out) {
+  philox4x32_10(ctr, key, out);
+}
+
+// k: fp16 bits [total_k, hk, d] contiguous, or NULL to read the INT8 cache k8 [total_k, hk, d]
+// with k_scale [total_k, hk].
+int oracle_route_topk_maxabs(const int32_t* cu_k, const int32_t* cu_mtiles, int32_t batch,
+                             int32_t hk, int32_t d, const uint16_t* k, const int8_t* k8,
+                             const float* k_scale, int32_t bn_r, int32_t group, int32_t per_mille,
+                             int32_t t_mask, uint8_t* R) {
+  int64_t span = 0;
+  if (check_route_args(cu_k, cu_mtiles, batch, hk, bn_r, group, per_mille, t_mask, R, &span)) return -1;
+  if (d < 1 || (!k && (!k8 || !k_scale))) return -1;
+  const double* f16 = binary16_table();
+  const int64_t total_mtiles = cu_mtiles[batch];
+  std::memset(R, 0, static_cast<size_t>(hk) * total_mtiles * t_mask);
+  for (int b = 0; b < batch; ++b) {
+    const int64_t k0 = cu_k[b], Lk = cu_k[b + 1] - cu_k[b];
+    const int64_t T = (Lk + span - 1) / span;
+    const int64_t nsel = (T * per_mille + 999) / 1000;
+    for (int h = 0; h < hk; ++h) {
+      std::vector<double> score(T, 0.0);
+      for (int64_t g = 0; g < T; ++g) {
+        for (int64_t j = g * span; j < std::min(Lk, (g + 1) * span); ++j) {
+          const int64_t row = ((k0 + j) * hk + h) * static_cast<int64_t>(d);
+          for (int c = 0; c < d; ++c) {
+            double a;
+            if (k) {
+              a = std::fabs(f16[k[row + c]]);
+            } else {
+              const float prod = k_scale[(k0 + j) * hk + h] * static_cast<float>(std::abs(static_cast<int>(k8[row + c])));
+              a = static_cast<double>(prod);
+            }
+            score[g] = std::max(score[g], a);
+          }
+        }
+      }
+      // descending max|K|; the stable sort keeps equal maxima in ascending group order
+      std::vector<int64_t> order(T);
+      for (int64_t g = 0; g < T; ++g) order[g] = g;
+      std::stable_sort(order.begin(), order.end(),
+                       [&](int64_t x, int64_t y) { return score[x] > score[y]; });
+      std::vector<uint8_t> bit(T, 1);
+      for (int64_t i = 0; i < nsel; ++i) bit[order[i]] = 0;
+      for (int64_t r = cu_mtiles[b]; r < cu_mtiles[b + 1]; ++r)
+        for (int64_t g = 0; g < T; ++g) R[(h * total_mtiles + r) * t_mask + g] = bit[g];
+    }
+  }
+  return 0;
+}
+
+int oracle_route_bernoulli(const int32_t* cu_k, const int32_t* cu_mtiles, int32_t batch,
+                           int32_t hk, int32_t bn_r, int32_t group, int32_t per_mille,
+                           uint64_t seed, int32_t t_mask, uint8_t* R) {
+  int64_t span = 0;
+  if (check_route_args(cu_k, cu_mtiles, batch, hk, bn_r, group, per_mille, t_mask, R, &span)) return -1;
+  const int64_t total_mtiles = cu_mtiles[batch];
+  const uint64_t thr = (static_cast<uint64_t>(per_mille) << 32) / 1000;
+  const uint32_t key[2] = {static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32)};
+  std::memset(R, 0, static_cast<size_t>(hk) * total_mtiles * t_mask);
+  for (int b = 0; b < batch; ++b) {
+    const int64_t T = (cu_k[b + 1] - cu_k[b] + span - 1) / span;
+    for (int h = 0; h < hk; ++h)
+      for (int64_t r = cu_mtiles[b]; r < cu_mtiles[b + 1]; ++r)
+        for (int64_t g = 0; g < T; ++g) {
+          const uint32_t ctr[4] = {static_cast<uint32_t>(g), static_cast<uint32_t>(r),
+                                   static_cast<uint32_t>(h), 0u};
+          uint32_t x[4];
+          philox4x32_10(ctr, key, x);
+          R[(h * total_mtiles + r) * t_mask + g] = x[0] < thr ? 0 : 1;
+        }
+  }
+  return 0;
+}
+
+}  // extern "C"
