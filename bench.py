@@ -35,6 +35,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_fwd_gqa32k_traffic.md")
 KERNEL_SRC = os.path.join(ROOT, "mixed_precision_attention_tilemix_amd", "csrc", "prefill_fwd.hip")
 DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_fwd_decode128k.md")
 DECODE_SRC = os.path.join(ROOT, "mixed_precision_attention_tilemix_amd", "csrc", "decode.hip")
+ROUTE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "route_topk_gqa32k.md")
+ROUTE_SRC = os.path.join(ROOT, "mixed_precision_attention_tilemix_amd", "csrc", "route.hip")
 
 
 def calibration_copy():
@@ -214,6 +216,109 @@ def run_decode(args):
     print(json.dumps(result), flush=True)
 
 
+ROUTE_WORKLOADS = {"route_gqa32k": ("gqa32k", 100)}
+
+
+def run_route(args):
+    """One step = tilemix_route_topk_maxabs on the 32k GQA workload's K (top 10 % max|K| groups
+    FP16), i.e. the on-device version of the policy that builds that workload's route map."""
+    import torch
+    from mixed_precision_attention_tilemix_amd import binding, workloads
+
+    binding.load()
+    base, per_mille = ROUTE_WORKLOADS[args.workload]
+    w = workloads.make(base)
+    dev = torch.device("cuda")
+    k = torch.from_numpy(w.k).to(dev)
+    cu = torch.from_numpy(w.cu_seqlens).to(dev)
+    cu_m = torch.from_numpy(w.cu_mtiles).to(dev)
+    words = torch.empty((w.hk, w.total_mtiles, w.words_per_row), dtype=torch.int64, device=dev)
+    L = max(w.seqlens)
+    nws = binding.tilemix_route_workspace_size(batch=w.batch, hkv=w.hk, max_seqlen_k=L,
+                                               route_block_n=w.bn_r, route_group=w.group)
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def topk():
+        binding.tilemix_route_topk_maxabs(cu_seqlens_k=cu, cu_mtiles=cu_m, max_seqlen_k=L,
+                                          route_block_n=w.bn_r, route_group=w.group,
+                                          fp16_per_mille=per_mille, route_words=words, workspace=ws, k=k)
+
+    def bern():
+        binding.tilemix_route_bernoulli(cu_seqlens_k=cu, cu_mtiles=cu_m, max_seqlen_k=L,
+                                        route_block_n=w.bn_r, route_group=w.group,
+                                        fp16_per_mille=per_mille, seed=1, route_words=words)
+
+    tmax = -(-L // (w.bn_r * w.group))
+    nbytes = (w.total * w.hk * w.d * 2 + words.numel() * 8 + 2 * 4 * w.batch * w.hk * tmax)
+    for _ in range(args.warmup):
+        topk()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(stream)
+        topk()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    got = words.cpu().numpy().view(np.uint64)
+    for e0, e1 in ev:
+        e0.record(stream)
+        bern()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    bern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    step_ms = wall * 1e3 / args.steps
+    result = {
+        "metric": "on-device top-k max|K| routing fused with packing: effective HBM bandwidth",
+        "value": round(nbytes / (step_ms * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16 keys, fp32 group maxima",
+        "data": "synthetic",
+        "config": dict(w.describe(), workload=args.workload, fp16_per_mille=per_mille),
+        "route_topk_ms": round(call_ms, 4),
+        "route_bernoulli_ms": round(bern_ms, 4),
+        "matches_host_route_map": None,
+        "roofline": {
+            "kernel": "group_maxabs_kernel<128,false> + topk_pack_kernel (the tilemix_route_topk_maxabs call)",
+            "bound": "hbm",
+            "achieved": round(nbytes / (call_ms * 1e-3) / 1e9, 1),
+            "peak": PEAK_HBM,
+            "unit": "GB/s",
+            "frac": round(nbytes / (call_ms * 1e-3) / 1e9 / PEAK_HBM, 4),
+            "traffic": measured_traffic(ROUTE_TRAFFIC_FILE, ROUTE_SRC),
+            "bytes_per_launch": nbytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        t1 = time.perf_counter()
+        R = oracle.route_topk_maxabs(w.cu_seqlens, w.cu_mtiles, w.hk, w.d, w.bn_r, w.group, per_mille,
+                                     k=w.k, t_mask=w.t_mask)
+        dt = time.perf_counter() - t1
+        want = oracle.pack_route(R, w.words_per_row)
+        result["matches_host_route_map"] = bool(np.array_equal(want, oracle.pack_route(w.route, w.words_per_row)))
+        result["cpu_baseline"] = {
+            "value": round(nbytes / dt / 1e9, 3),
+            "unit": "GB/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"the whole step (top-k policy over all {w.total} keys x {w.hk} KV heads), {dt:.2f} s",
+            "seconds": dt,
+            "parity_words_equal": bool(np.array_equal(got, want)),
+        }
+    print(json.dumps(result), flush=True)
+
+
 def exact_attention_cpu(w):
     """Causal softmax attention of the fp16 inputs in fp64 with plain PyTorch CPU ops: the
     reference of the deviation sweep (independent of the routed kernel and of the oracle)."""
@@ -296,6 +401,9 @@ def main():
     from mixed_precision_attention_tilemix_amd import workloads as _wl
     if args.workload == "numerics":
         run_numerics(args)
+        return
+    if args.workload in ROUTE_WORKLOADS:
+        run_route(args)
         return
     if args.workload in _wl.DECODE_WORKLOADS:
         run_decode(args)

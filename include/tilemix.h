@@ -199,6 +199,88 @@ tilemix_status tilemix_decode_workspace_size(const tilemix_fwd_params* params, i
  */
 tilemix_status tilemix_decode_fwd(const tilemix_fwd_params* params, void* stream);
 
+/*
+ * Routing policies on the device, fused with packing. The pages let the caller supply the routing
+ * map R from any static or adaptive policy (Section 4.2, "Policy definition"; Limitations); these
+ * calls compute R for one of two policies and write it straight into route words of the layout
+ * tilemix_pack_route_mask produces ([hkv, total_mtiles, words_per_row], group g_j in word
+ * g_j >> 6 at bit g_j & 63), ready for tilemix_prefill_fwd / tilemix_decode_fwd with the same
+ * route geometry. For sequence b, T_b = ceil(L_k,b / (route_block_n * route_group)) groups exist;
+ * bits at or past T_b are 0.
+ *
+ * fp16_per_mille sets the FP16 budget (the INT8 coverage is its complement):
+ *   - top-k max|K| (tilemix_route_topk_maxabs): per sequence b and KV head h_k, the
+ *     ceil(T_b * fp16_per_mille / 1000) groups with the largest max|K| over their keys and
+ *     channels take the FP16 path (bit 0) in every route row of b (cu_mtiles[b] ..
+ *     cu_mtiles[b+1]); ties go to the lower group index; the other groups below T_b are INT8
+ *     (bit 1). |K| is the fp16 value, or with kv_int8 the fp32 product k_scale * |k8|. Inputs
+ *     must be finite. A deterministic, data-dependent policy: the 32k GQA setting's
+ *     "largest max|K| groups in FP16".
+ *   - coverage-budget Bernoulli (tilemix_route_bernoulli): bit (h_k, route row r, g_j < T_b) is 0
+ *     (FP16) iff x < floor(fp16_per_mille * 2^32 / 1000), x the first output word of
+ *     Philox4x32-10 (Salmon et al., SC 2011) at counter (g_j, r, h_k, 0) and key (seed & 0xffffffff,
+ *     seed >> 32); a data-free layout, reproducible from the seed.
+ */
+typedef struct tilemix_route_params {
+  uint32_t struct_size;         /* sizeof(tilemix_route_params) */
+  int32_t batch;                /* sequences, 1 .. 65535 */
+  int32_t hkv;                  /* KV heads (route rows are per KV head), 1 .. 65535 */
+  int32_t head_dim;             /* 64 or 128 (top-k only) */
+  int32_t max_seqlen_k;         /* >= every L_k,b */
+  const int32_t* cu_seqlens_k;  /* device [batch+1], prefix sums of L_k,b */
+  const int32_t* cu_mtiles;     /* device [batch+1], prefix sums of route rows per sequence */
+  int32_t total_mtiles;         /* cu_mtiles[batch] */
+  int32_t route_block_n;        /* BN_r, positive multiple of 64 */
+  int32_t route_group;          /* g >= 1 */
+  int32_t fp16_per_mille;       /* FP16 budget, 0 .. 1000 */
+
+  /* top-k only: the keys, fp16 [total_k, hkv, d] (strided, multiples of 8 elements, 16-byte
+   * aligned) with k8 / k_scale NULL, or (kv_int8 = 1) the INT8 cache k8 [total_k, hkv, d]
+   * (16-byte aligned) with k_scale [hkv, total_k] and k NULL. */
+  const void* k;
+  int64_t k_stride_tok, k_stride_head;
+  const int8_t* k8;
+  const float* k_scale;
+  int64_t total_k;
+  int32_t kv_int8;
+
+  uint64_t seed;                /* Bernoulli only */
+
+  uint64_t* route_words;        /* output [hkv, total_mtiles, words_per_row], 8-byte aligned */
+  int32_t words_per_row;        /* >= ceil(ceil(max_seqlen_k / (BN_r * g)) / 64) */
+
+  /* top-k only: device scratch of tilemix_route_workspace_size() bytes, 256-byte aligned,
+   * caller-owned (per-group maxima); calls sharing it must not overlap in time. */
+  void* workspace;
+  int64_t workspace_bytes;
+} tilemix_route_params;
+
+/*
+ * tilemix_route_workspace_size - bytes of workspace tilemix_route_topk_maxabs needs (batch, hkv,
+ * max_seqlen_k, route_block_n and route_group are read): 4 * batch * hkv * ceil(max_seqlen_k /
+ * (BN_r * g)), rounded up to 256. Errors: EINVAL for NULL arguments or out-of-range sizes.
+ */
+tilemix_status tilemix_route_workspace_size(const tilemix_route_params* params, int64_t* bytes);
+
+/*
+ * tilemix_route_topk_maxabs - the top-k max|K| policy above. A group-maximum pass (one workgroup
+ * per (group, KV head, sequence), reading every key once) fills the workspace; a select-and-pack
+ * pass (one workgroup per (KV head, sequence)) ranks the groups and writes the words of every
+ * route row. Both are enqueued on `stream`; the result is bitwise deterministic.
+ * Errors: EINVAL for a NULL or misaligned pointer, struct_size mismatch, bad strides, a budget
+ * outside 0..1000, route_block_n / route_group / words_per_row out of range, a missing or small
+ * workspace, k and k8 both or neither set; EUNSUPPORTED for head_dim other than 64/128 or more
+ * than 8192 groups per sequence.
+ */
+tilemix_status tilemix_route_topk_maxabs(const tilemix_route_params* params, void* stream);
+
+/*
+ * tilemix_route_bernoulli - the coverage-budget Bernoulli policy above (k, k8, k_scale, head_dim
+ * and the workspace are not read). One wavefront per route word, one lane per group. Errors:
+ * EINVAL as for the top-k call where the fields apply.
+ */
+tilemix_status tilemix_route_bernoulli(const tilemix_route_params* params, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

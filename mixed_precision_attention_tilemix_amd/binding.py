@@ -24,7 +24,8 @@ TILEMIX_OK, TILEMIX_EINVAL, TILEMIX_EUNSUPPORTED, TILEMIX_ELAUNCH = 0, 1, 2, 3
 # The entry points declared in include/tilemix.h.
 EXPORTED = ("tilemix_last_error", "tilemix_version", "tilemix_quantize_qk",
             "tilemix_pack_route_mask", "tilemix_prefill_workspace_size", "tilemix_prefill_fwd",
-            "tilemix_decode_workspace_size", "tilemix_decode_fwd")
+            "tilemix_decode_workspace_size", "tilemix_decode_fwd", "tilemix_route_workspace_size",
+            "tilemix_route_topk_maxabs", "tilemix_route_bernoulli")
 
 
 class TilemixError(RuntimeError):
@@ -67,6 +68,25 @@ class FwdParams(ctypes.Structure):
     ]
 
 
+class RouteParams(ctypes.Structure):
+    """Mirror of tilemix_route_params."""
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("batch", ctypes.c_int32), ("hkv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("max_seqlen_k", ctypes.c_int32),
+        ("cu_seqlens_k", ctypes.c_void_p), ("cu_mtiles", ctypes.c_void_p),
+        ("total_mtiles", ctypes.c_int32),
+        ("route_block_n", ctypes.c_int32), ("route_group", ctypes.c_int32),
+        ("fp16_per_mille", ctypes.c_int32),
+        ("k", ctypes.c_void_p), ("k_stride_tok", ctypes.c_int64), ("k_stride_head", ctypes.c_int64),
+        ("k8", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
+        ("total_k", ctypes.c_int64), ("kv_int8", ctypes.c_int32),
+        ("seed", ctypes.c_uint64),
+        ("route_words", ctypes.c_void_p), ("words_per_row", ctypes.c_int32),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64),
+    ]
+
+
 def load(path: Optional[str] = None):
     """Load libtilemix.so (once). Raises FileNotFoundError if it has not been built."""
     global _lib
@@ -95,6 +115,11 @@ def load(path: Optional[str] = None):
     L.tilemix_decode_workspace_size.argtypes = [ctypes.POINTER(FwdParams), ctypes.POINTER(ctypes.c_int64)]
     L.tilemix_decode_fwd.restype = ctypes.c_int
     L.tilemix_decode_fwd.argtypes = [ctypes.POINTER(FwdParams), vp]
+    for name in ("tilemix_route_topk_maxabs", "tilemix_route_bernoulli"):
+        getattr(L, name).restype = ctypes.c_int
+        getattr(L, name).argtypes = [ctypes.POINTER(RouteParams), vp]
+    L.tilemix_route_workspace_size.restype = ctypes.c_int
+    L.tilemix_route_workspace_size.argtypes = [ctypes.POINTER(RouteParams), ctypes.POINTER(ctypes.c_int64)]
     _lib = L
     return L
 
@@ -257,3 +282,66 @@ def tilemix_decode_fwd(*, q, q8, q_scale, k8, k_scale, v8, v_scale, route_words,
                     v_scale=v_scale, causal=causal, softmax_scale=softmax_scale, lse=lse,
                     debug_s32=None, debug_head=0, debug_mtile_begin=0, debug_mtile_count=0)
     _check(load().tilemix_decode_fwd(ctypes.byref(p), _stream(stream)))
+
+
+def tilemix_route_workspace_size(*, batch: int, hkv: int, max_seqlen_k: int, route_block_n: int,
+                                 route_group: int) -> int:
+    """Bytes of device workspace tilemix_route_topk_maxabs needs."""
+    p = RouteParams()
+    p.struct_size = ctypes.sizeof(RouteParams)
+    p.batch, p.hkv, p.max_seqlen_k = batch, hkv, max_seqlen_k
+    p.route_block_n, p.route_group = route_block_n, route_group
+    out = ctypes.c_int64(0)
+    _check(load().tilemix_route_workspace_size(ctypes.byref(p), ctypes.byref(out)))
+    return out.value
+
+
+def _route_params(*, cu_seqlens_k, cu_mtiles, max_seqlen_k, route_block_n, route_group,
+                  fp16_per_mille, route_words, hkv, head_dim=0, k=None, k8=None, k_scale=None,
+                  seed=0, workspace=None) -> RouteParams:
+    p = RouteParams()
+    p.struct_size = ctypes.sizeof(RouteParams)
+    p.batch = cu_seqlens_k.shape[0] - 1
+    p.hkv = hkv
+    p.head_dim = head_dim
+    p.max_seqlen_k = int(max_seqlen_k)
+    p.cu_seqlens_k, p.cu_mtiles = _ptr(cu_seqlens_k), _ptr(cu_mtiles)
+    p.total_mtiles = route_words.shape[1]
+    p.route_block_n, p.route_group = route_block_n, route_group
+    p.fp16_per_mille = int(fp16_per_mille)
+    if k is not None:
+        p.k, (p.k_stride_tok, p.k_stride_head) = _ptr(k), _tok_head_strides(k)
+        p.total_k = k.shape[0]
+    if k8 is not None:
+        p.k8, p.k_scale, p.kv_int8 = _ptr(k8), _ptr(k_scale), 1
+        p.total_k = k8.shape[0]
+    p.seed = int(seed) & 0xFFFFFFFFFFFFFFFF
+    p.route_words, p.words_per_row = _ptr(route_words), route_words.shape[2]
+    p.workspace = _ptr(workspace)
+    p.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return p
+
+
+def tilemix_route_topk_maxabs(*, cu_seqlens_k, cu_mtiles, max_seqlen_k: int, route_block_n: int,
+                              route_group: int, fp16_per_mille: int, route_words, workspace,
+                              k=None, k8=None, k_scale=None, stream=None) -> None:
+    """Top-k max|K| routing written as route words [hkv, total_mtiles, words_per_row].
+
+    k: fp16 [T, hkv, d] (strided); or k8 int8 [T, hkv, d] with k_scale fp32 [hkv, T]."""
+    ref = k if k is not None else k8
+    p = _route_params(cu_seqlens_k=cu_seqlens_k, cu_mtiles=cu_mtiles, max_seqlen_k=max_seqlen_k,
+                      route_block_n=route_block_n, route_group=route_group,
+                      fp16_per_mille=fp16_per_mille, route_words=route_words, hkv=ref.shape[1],
+                      head_dim=ref.shape[2], k=k, k8=k8, k_scale=k_scale, workspace=workspace)
+    _check(load().tilemix_route_topk_maxabs(ctypes.byref(p), _stream(stream)))
+
+
+def tilemix_route_bernoulli(*, cu_seqlens_k, cu_mtiles, max_seqlen_k: int, route_block_n: int,
+                            route_group: int, fp16_per_mille: int, seed: int, route_words,
+                            stream=None) -> None:
+    """Coverage-budget Bernoulli routing (Philox4x32-10) written as route words."""
+    p = _route_params(cu_seqlens_k=cu_seqlens_k, cu_mtiles=cu_mtiles, max_seqlen_k=max_seqlen_k,
+                      route_block_n=route_block_n, route_group=route_group,
+                      fp16_per_mille=fp16_per_mille, route_words=route_words,
+                      hkv=route_words.shape[0], seed=seed)
+    _check(load().tilemix_route_bernoulli(ctypes.byref(p), _stream(stream)))

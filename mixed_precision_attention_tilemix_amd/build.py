@@ -9,7 +9,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtilemix.so")
-SOURCES = ["api.cpp", "quantize.hip", "pack.hip", "vt_pack.hip", "prefill_fwd.hip", "decode.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "pack.hip", "vt_pack.hip", "prefill_fwd.hip", "decode.hip", "route.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -180,6 +180,63 @@ tilemix_status check_params(const tilemix_fwd_params* p, const char* fn) {
   return TILEMIX_OK;
 }
 
+// Checks shared by the two routing policies; *tmax = ceil(max_seqlen_k / (BN_r * g)).
+tilemix_status check_route(const tilemix_route_params* p, const char* fn, int64_t* tmax) {
+  if (p == nullptr) return fail(TILEMIX_EINVAL, "%s: NULL params", fn);
+  if (p->struct_size != sizeof(tilemix_route_params))
+    return fail(TILEMIX_EINVAL, "%s: struct_size %u != %zu", fn, p->struct_size,
+                sizeof(tilemix_route_params));
+  if (p->batch < 1 || p->batch > 65535 || p->hkv < 1 || p->hkv > 65535)
+    return fail(TILEMIX_EINVAL, "%s: batch=%d hkv=%d (each 1 .. 65535)", fn, p->batch, p->hkv);
+  if (p->max_seqlen_k < 0 || p->total_mtiles < 0) return fail(TILEMIX_EINVAL, "%s: negative size", fn);
+  if (p->route_block_n < 64 || p->route_block_n % 64)
+    return fail(TILEMIX_EINVAL, "%s: route_block_n %d is not a positive multiple of 64", fn, p->route_block_n);
+  if (p->route_group < 1) return fail(TILEMIX_EINVAL, "%s: route_group %d < 1", fn, p->route_group);
+  if (p->fp16_per_mille < 0 || p->fp16_per_mille > 1000)
+    return fail(TILEMIX_EINVAL, "%s: fp16_per_mille %d outside 0 .. 1000", fn, p->fp16_per_mille);
+  if (p->words_per_row < 1) return fail(TILEMIX_EINVAL, "%s: words_per_row < 1", fn);
+  *tmax = ceil_div(p->max_seqlen_k, static_cast<int64_t>(p->route_block_n) * p->route_group);
+  if (*tmax > 64LL * p->words_per_row)
+    return fail(TILEMIX_EINVAL, "%s: %lld key-tile groups need more than %d words per row", fn,
+                (long long)*tmax, p->words_per_row);
+  if (!p->cu_seqlens_k || !p->cu_mtiles || !p->route_words)
+    return fail(TILEMIX_EINVAL, "%s: a required pointer is NULL", fn);
+  if (!aligned(p->route_words, 8)) return fail(TILEMIX_EINVAL, "%s: route_words misaligned", fn);
+  if (static_cast<int64_t>(p->hkv) * p->total_mtiles * p->words_per_row >= (int64_t{1} << 33))
+    return fail(TILEMIX_EINVAL, "%s: too many route words", fn);
+  return TILEMIX_OK;
+}
+
+int64_t route_workspace(const tilemix_route_params* p) {
+  const int64_t tmax = ceil_div(p->max_seqlen_k, static_cast<int64_t>(p->route_block_n) * p->route_group);
+  return round_up(int64_t{4} * p->batch * p->hkv * tmax, 256);
+}
+
+tilemix::RouteArgs route_args(const tilemix_route_params* p, int64_t tmax) {
+  tilemix::RouteArgs a{};
+  a.batch = p->batch;
+  a.hkv = p->hkv;
+  a.cu_k = p->cu_seqlens_k;
+  a.cu_mtiles = p->cu_mtiles;
+  a.total_mtiles = p->total_mtiles;
+  a.span = static_cast<int64_t>(p->route_block_n) * p->route_group;
+  a.tmax = static_cast<int32_t>(tmax);
+  a.per_mille = p->fp16_per_mille;
+  a.k = static_cast<const uint16_t*>(p->k);
+  a.k_stride_tok = p->k_stride_tok;
+  a.k_stride_head = p->k_stride_head;
+  a.k8 = p->k8;
+  a.k_scale = p->k_scale;
+  a.total_k = p->total_k;
+  a.seed_lo = static_cast<uint32_t>(p->seed);
+  a.seed_hi = static_cast<uint32_t>(p->seed >> 32);
+  a.thr = (static_cast<uint64_t>(p->fp16_per_mille) << 32) / 1000;
+  a.words = p->route_words;
+  a.wpr = p->words_per_row;
+  a.gmax = static_cast<float*>(p->workspace);
+  return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -308,6 +365,53 @@ tilemix_status tilemix_decode_fwd(const tilemix_fwd_params* p, void* stream) {
   d.rmax = (p->hq / p->hkv) * p->max_seqlen_q;
   return from_hip(tilemix::launch_decode(d, p->batch, p->head_dim, static_cast<hipStream_t>(stream)),
                   "decode_fwd");
+}
+
+tilemix_status tilemix_route_workspace_size(const tilemix_route_params* p, int64_t* bytes) {
+  if (p == nullptr || bytes == nullptr) return fail(TILEMIX_EINVAL, "route_workspace_size: NULL argument");
+  if (p->batch < 1 || p->hkv < 1 || p->max_seqlen_k < 0 || p->route_block_n < 1 || p->route_group < 1)
+    return fail(TILEMIX_EINVAL, "route_workspace_size: batch=%d hkv=%d max_seqlen_k=%d route_block_n=%d route_group=%d",
+                p->batch, p->hkv, p->max_seqlen_k, p->route_block_n, p->route_group);
+  *bytes = route_workspace(p);
+  return ok();
+}
+
+tilemix_status tilemix_route_topk_maxabs(const tilemix_route_params* p, void* stream) {
+  int64_t tmax = 0;
+  if (tilemix_status st = check_route(p, "route_topk_maxabs", &tmax)) return st;
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(TILEMIX_EUNSUPPORTED, "route_topk_maxabs: head_dim %d (supported: 64, 128)", p->head_dim);
+  if (tmax > tilemix::kRouteMaxGroups)
+    return fail(TILEMIX_EUNSUPPORTED, "route_topk_maxabs: %lld groups per sequence > %d", (long long)tmax,
+                tilemix::kRouteMaxGroups);
+  if (p->kv_int8) {
+    if (p->k || !p->k8 || !p->k_scale)
+      return fail(TILEMIX_EINVAL, "route_topk_maxabs: kv_int8 reads k8 and k_scale; k must be NULL");
+    if (p->total_k < 0) return fail(TILEMIX_EINVAL, "route_topk_maxabs: negative total_k");
+    if (!aligned(p->k8, 16) || !aligned(p->k_scale, 4))
+      return fail(TILEMIX_EINVAL, "route_topk_maxabs: k8 / k_scale misaligned (16 / 4 bytes)");
+  } else {
+    if (!p->k || p->k8 || p->k_scale)
+      return fail(TILEMIX_EINVAL, "route_topk_maxabs: fp16 keys are read from k; k8 and k_scale must be NULL");
+    if (p->k_stride_tok < 0 || p->k_stride_head < 0 || p->k_stride_tok % 8 || p->k_stride_head % 8)
+      return fail(TILEMIX_EINVAL, "route_topk_maxabs: k strides must be non-negative multiples of 8");
+    if (!aligned(p->k, 16)) return fail(TILEMIX_EINVAL, "route_topk_maxabs: k must be 16-byte aligned");
+  }
+  const int64_t need = route_workspace(p);
+  if (need > 0 && (p->workspace == nullptr || !aligned(p->workspace, 256) || p->workspace_bytes < need))
+    return fail(TILEMIX_EINVAL, "route_topk_maxabs: workspace must be 256-byte aligned and hold %lld bytes (got %lld)",
+                (long long)need, (long long)p->workspace_bytes);
+  if (p->total_mtiles == 0) return ok();
+  return from_hip(tilemix::launch_route_topk(route_args(p, tmax), p->head_dim, p->kv_int8 != 0,
+                                             static_cast<hipStream_t>(stream)),
+                  "route_topk_maxabs");
+}
+
+tilemix_status tilemix_route_bernoulli(const tilemix_route_params* p, void* stream) {
+  int64_t tmax = 0;
+  if (tilemix_status st = check_route(p, "route_bernoulli", &tmax)) return st;
+  return from_hip(tilemix::launch_route_bernoulli(route_args(p, tmax), static_cast<hipStream_t>(stream)),
+                  "route_bernoulli");
 }
 
 }  // extern "C"

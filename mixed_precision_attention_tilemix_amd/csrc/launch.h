@@ -75,4 +75,31 @@ struct DecodeArgs {
 // Chunk pass then merge pass, both on `stream`.
 hipError_t launch_decode(const DecodeArgs& a, int32_t batch, int32_t head_dim, hipStream_t stream);
 
+// Routing policies fused with packing. Groups per sequence are at most kRouteMaxGroups for the
+// top-k policy (its select pass ranks them in LDS).
+constexpr int kRouteMaxGroups = 8192;
+
+struct RouteArgs {
+  int32_t batch, hkv;
+  const int32_t* cu_k;
+  const int32_t* cu_mtiles;
+  int32_t total_mtiles;
+  int64_t span;          // keys per routing group: BN_r * g
+  int32_t tmax;          // ceil(max_seqlen_k / span): group slots per (sequence, KV head)
+  int32_t per_mille;     // FP16 budget
+  const uint16_t* k;     // fp16 bits, or NULL with the INT8 cache
+  int64_t k_stride_tok, k_stride_head;
+  const int8_t* k8;      // [total_k, hkv, D]
+  const float* k_scale;  // [hkv, total_k]
+  int64_t total_k;
+  uint32_t seed_lo, seed_hi;
+  uint64_t thr;          // Bernoulli: FP16 iff Philox word < thr
+  uint64_t* words;       // [hkv, total_mtiles, wpr]
+  int32_t wpr;
+  float* gmax;           // top-k workspace [batch][hkv][tmax]
+};
+
+hipError_t launch_route_topk(const RouteArgs& a, int32_t head_dim, bool kv_int8, hipStream_t stream);
+hipError_t launch_route_bernoulli(const RouteArgs& a, hipStream_t stream);
+
 }  // namespace tilemix

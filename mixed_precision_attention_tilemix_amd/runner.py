@@ -15,13 +15,17 @@ class DeviceProblem:
     """A workload resident in device memory plus its outputs.
 
     ``step()`` is one pass of the hot path: tilemix_quantize_qk (Q, and K unless K/V arrive as
-    an INT8 cache), tilemix_pack_route_mask and tilemix_prefill_fwd, all enqueued on the current
-    stream. With ``kv_int8`` the INT8 K/V cache is produced once at construction by the library's
+    an INT8 cache), the route words, and tilemix_prefill_fwd, all enqueued on the current
+    stream. The route words come from tilemix_pack_route_mask of the workload's routing map, or,
+    with ``route_policy``, from an on-device policy computed in the step:
+    ``("topk_maxabs", fp16_per_mille)`` or ``("bernoulli", fp16_per_mille, seed)``.
+    With ``kv_int8`` the INT8 K/V cache is produced once at construction by the library's
     own quantizer, and the fp16 K/V are dropped."""
 
     def __init__(self, w, device: str = "cuda", out_dtype=torch.float32, with_lse: bool = True,
-                 softmax_scale: float = 0.0):
+                 softmax_scale: float = 0.0, route_policy: Optional[tuple] = None):
         self.w = w
+        self.route_policy = route_policy
         dev = torch.device(device)
         T, hq, hk, d = w.total, w.hq, w.hk, w.d
         self.q = torch.from_numpy(w.q).to(dev)
@@ -40,6 +44,11 @@ class DeviceProblem:
         ws_bytes = B.tilemix_prefill_workspace_size(batch=w.batch, hkv=hk, head_dim=d, total_k=T,
                                                     kv_int8=w.kv_int8)
         self.workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+        self.route_ws = None
+        if route_policy is not None and route_policy[0] == "topk_maxabs":
+            n = B.tilemix_route_workspace_size(batch=w.batch, hkv=hk, max_seqlen_k=max(w.seqlens),
+                                               route_block_n=w.bn_r, route_group=w.group)
+            self.route_ws = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
         if w.kv_int8:
             k = torch.from_numpy(w.k).to(dev)
             v = torch.from_numpy(w.v).to(dev)
@@ -65,6 +74,26 @@ class DeviceProblem:
         B.tilemix_pack_route_mask(self.route.view(-1, self.route.shape[-1]),
                                   self.words.view(-1, self.words.shape[-1]), stream=stream)
 
+    def route_words(self, stream=None):
+        """Fill the route words: pack the workload's map, or run the on-device policy."""
+        pol = self.route_policy
+        if pol is None:
+            self.pack(stream)
+            return
+        w = self.w
+        common = dict(cu_seqlens_k=self.cu, cu_mtiles=self.cu_mtiles, max_seqlen_k=self.max_seqlen,
+                      route_block_n=w.bn_r, route_group=w.group, fp16_per_mille=pol[1],
+                      route_words=self.words, stream=stream)
+        if pol[0] == "topk_maxabs":
+            if w.kv_int8:
+                B.tilemix_route_topk_maxabs(k8=self.k8, k_scale=self.k_scale, workspace=self.route_ws, **common)
+            else:
+                B.tilemix_route_topk_maxabs(k=self.k, workspace=self.route_ws, **common)
+        elif pol[0] == "bernoulli":
+            B.tilemix_route_bernoulli(seed=pol[2], **common)
+        else:
+            raise ValueError(f"unknown route policy {pol[0]!r}")
+
     def attention(self, stream=None, debug_s32: Optional[torch.Tensor] = None, debug_head: int = 0,
                   debug_mtile_begin: int = 0, debug_mtile_count: int = 0):
         w = self.w
@@ -81,7 +110,7 @@ class DeviceProblem:
 
     def step(self, stream=None):
         self.quantize(stream)
-        self.pack(stream)
+        self.route_words(stream)
         self.attention(stream)
 
 

@@ -225,3 +225,111 @@ def test_decode_workspace_size(lib):
     p.head_dim, p.hkv = 128, 3
     assert lib.tilemix_decode_workspace_size(ctypes.byref(p), ctypes.byref(n)) == B.TILEMIX_EINVAL
     assert lib.tilemix_decode_workspace_size(None, ctypes.byref(n)) == B.TILEMIX_EINVAL
+
+
+def test_route_struct_matches_c_layout(tmp_path):
+    fields = [f for f, _ in B.RouteParams._fields_]
+    src = tmp_path / "route_layout.c"
+    body = "\n".join(f'  printf("%s %zu\\n", "{f}", offsetof(tilemix_route_params, {f}));' for f in fields)
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "tilemix.h"\nint main(void){\n'
+                   '  printf("sizeof %zu\\n", sizeof(tilemix_route_params));\n' + body + "\n  return 0;\n}\n")
+    exe = tmp_path / "route_layout"
+    subprocess.check_call(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
+    got = dict(line.split() for line in subprocess.check_output([str(exe)], text=True).splitlines())
+    assert int(got["sizeof"]) == ctypes.sizeof(B.RouteParams)
+    for f in fields:
+        assert int(got[f]) == getattr(B.RouteParams, f).offset, f
+
+
+def route_params(kv_int8=False):
+    """A valid top-k routing call: 2 sequences, 2 KV heads, 4096 keys, 64 x 2 key groups."""
+    p = B.RouteParams()
+    p.struct_size = ctypes.sizeof(B.RouteParams)
+    p.batch, p.hkv, p.head_dim = 2, 2, 128
+    p.max_seqlen_k = 4096
+    p.cu_seqlens_k = p.cu_mtiles = FAKE
+    p.total_mtiles = 40
+    p.route_block_n, p.route_group = 64, 2
+    p.fp16_per_mille = 100
+    if kv_int8:
+        p.k8 = p.k_scale = FAKE
+        p.kv_int8 = 1
+        p.total_k = 6000
+    else:
+        p.k = FAKE
+        p.k_stride_tok, p.k_stride_head = 256, 128
+    p.route_words = FAKE
+    p.words_per_row = 1
+    p.workspace = FAKE
+    p.workspace_bytes = 1 << 20
+    return p
+
+
+ROUTE_BAD_CASES = [
+    ("struct_size", lambda p: setattr(p, "struct_size", 4), B.TILEMIX_EINVAL),
+    ("batch", lambda p: setattr(p, "batch", 0), B.TILEMIX_EINVAL),
+    ("hkv", lambda p: setattr(p, "hkv", 70000), B.TILEMIX_EINVAL),
+    ("route_block_n", lambda p: setattr(p, "route_block_n", 32), B.TILEMIX_EINVAL),
+    ("route_group", lambda p: setattr(p, "route_group", 0), B.TILEMIX_EINVAL),
+    ("budget high", lambda p: setattr(p, "fp16_per_mille", 1001), B.TILEMIX_EINVAL),
+    ("budget negative", lambda p: setattr(p, "fp16_per_mille", -1), B.TILEMIX_EINVAL),
+    ("too many groups", lambda p: setattr(p, "max_seqlen_k", 128 * 65), B.TILEMIX_EINVAL),
+    ("null words", lambda p: setattr(p, "route_words", None), B.TILEMIX_EINVAL),
+    ("misaligned words", lambda p: setattr(p, "route_words", FAKE + 4), B.TILEMIX_EINVAL),
+    ("null cu", lambda p: setattr(p, "cu_mtiles", None), B.TILEMIX_EINVAL),
+]
+
+TOPK_BAD_CASES = ROUTE_BAD_CASES + [
+    ("head_dim", lambda p: setattr(p, "head_dim", 96), B.TILEMIX_EUNSUPPORTED),
+    ("groups past LDS", lambda p: (setattr(p, "max_seqlen_k", 64 * 2 * 8193), setattr(p, "words_per_row", 129)),
+     B.TILEMIX_EUNSUPPORTED),
+    ("k and k8", lambda p: setattr(p, "k8", FAKE), B.TILEMIX_EINVAL),
+    ("no keys", lambda p: setattr(p, "k", None), B.TILEMIX_EINVAL),
+    ("odd stride", lambda p: setattr(p, "k_stride_tok", 100), B.TILEMIX_EINVAL),
+    ("misaligned k", lambda p: setattr(p, "k", FAKE + 8), B.TILEMIX_EINVAL),
+    ("null workspace", lambda p: setattr(p, "workspace", None), B.TILEMIX_EINVAL),
+    ("small workspace", lambda p: setattr(p, "workspace_bytes", 64), B.TILEMIX_EINVAL),
+    ("misaligned workspace", lambda p: setattr(p, "workspace", FAKE + 64), B.TILEMIX_EINVAL),
+]
+
+
+@pytest.mark.parametrize("name,mutate,status", TOPK_BAD_CASES, ids=[c[0] for c in TOPK_BAD_CASES])
+def test_route_topk_validation(lib, name, mutate, status):
+    p = route_params()
+    mutate(p)
+    assert lib.tilemix_route_topk_maxabs(ctypes.byref(p), None) == status, (name, B.last_error())
+    assert B.last_error().startswith("route_topk_maxabs")
+
+
+def test_route_topk_int8_cache_validation(lib):
+    for mutate in (lambda p: setattr(p, "k", FAKE), lambda p: setattr(p, "k_scale", None),
+                   lambda p: setattr(p, "k8", FAKE + 8), lambda p: setattr(p, "total_k", -1)):
+        p = route_params(kv_int8=True)
+        mutate(p)
+        assert lib.tilemix_route_topk_maxabs(ctypes.byref(p), None) == B.TILEMIX_EINVAL, B.last_error()
+
+
+@pytest.mark.parametrize("name,mutate,status", ROUTE_BAD_CASES, ids=[c[0] for c in ROUTE_BAD_CASES])
+def test_route_bernoulli_validation(lib, name, mutate, status):
+    p = route_params()
+    p.k = None  # the Bernoulli policy reads no keys and no workspace
+    p.workspace = None
+    mutate(p)
+    assert lib.tilemix_route_bernoulli(ctypes.byref(p), None) == status, (name, B.last_error())
+    assert B.last_error().startswith("route_bernoulli")
+
+
+def test_route_null_params_and_workspace_size(lib):
+    assert lib.tilemix_route_topk_maxabs(None, None) == B.TILEMIX_EINVAL
+    assert lib.tilemix_route_bernoulli(None, None) == B.TILEMIX_EINVAL
+    p = route_params()
+    n = ctypes.c_int64(0)
+    assert lib.tilemix_route_workspace_size(ctypes.byref(p), ctypes.byref(n)) == B.TILEMIX_OK
+    # 4 bytes x batch 2 x hkv 2 x ceil(4096 / 128) groups, rounded up to 256
+    assert n.value == 512
+    p.max_seqlen_k = 0
+    assert lib.tilemix_route_workspace_size(ctypes.byref(p), ctypes.byref(n)) == B.TILEMIX_OK
+    assert n.value == 0
+    p.route_group = 0
+    assert lib.tilemix_route_workspace_size(ctypes.byref(p), ctypes.byref(n)) == B.TILEMIX_EINVAL
+    assert lib.tilemix_route_workspace_size(None, ctypes.byref(n)) == B.TILEMIX_EINVAL
