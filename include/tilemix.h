@@ -101,8 +101,8 @@ typedef struct tilemix_fwd_params {
   const void* v;                /* fp16 [total_k, hkv, d] (strided); NULL iff kv_int8 */
   int64_t v_stride_tok, v_stride_head;
 
-  const int8_t* q8;             /* [total_q, hq, d], from tilemix_quantize_qk */
-  const float* q_scale;         /* [hq, total_q] */
+  const int8_t* q8;             /* [total_q, hq, d], from tilemix_quantize_qk; or NULL together */
+  const float* q_scale;         /* [hq, total_q]     with q_scale: the kernel quantizes Q itself */
   const int8_t* k8;             /* [total_k, hkv, d] */
   const float* k_scale;         /* [hkv, total_k] */
   const int8_t* v8;             /* [total_k, hkv, d]; kv_int8 only (V = v_scale * v8) */
@@ -160,6 +160,11 @@ tilemix_status tilemix_prefill_workspace_size(const tilemix_fwd_params* params, 
  * gets O = 0 and LSE = -inf. Scores, softmax state and the P.V accumulator are fp32; P is
  * rounded to fp16 for the FP16 P.V product.
  *
+ * Q quantization: with q8 / q_scale set, the INT8 path reads the codes of the quantize-once pass
+ * (Section 4.3, "quantize-once mode"). With both NULL the fused kernel quantizes each query row
+ * when it loads it, with the same arithmetic as tilemix_quantize_qk (per-token symmetric,
+ * bit-identical codes and scales), so the separate Q pass is skipped. One NULL is EINVAL.
+ *
  * Implementation: a pre-pass writes V^T tiles (and, with kv_int8, fp16 K) into the workspace,
  * then the fused kernel runs; both are enqueued on `stream`.
  *
@@ -185,6 +190,8 @@ tilemix_status tilemix_decode_workspace_size(const tilemix_fwd_params* params, i
  * Section 4.3 routed scores). With max_seqlen_q <= 8 every query of a sequence reads route row
  * cu_mtiles[b] (route_block_m >= 32).
  *
+ * q8 / q_scale may both be NULL, as for tilemix_prefill_fwd: each chunk workgroup then
+ * quantizes its query rows itself, bit-identically to tilemix_quantize_qk.
  * Requirements beyond tilemix_prefill_fwd: kv_int8 = 1 (k, v NULL; k8, k_scale, v8, v_scale
  * set), max_seqlen_q <= 8 and (hq / hkv) * max_seqlen_q <= 16 (EUNSUPPORTED otherwise),
  * debug_s32 NULL (EINVAL), and a workspace of tilemix_decode_workspace_size() bytes,

@@ -154,9 +154,11 @@ tilemix_status check_params(const tilemix_fwd_params* p, const char* fn) {
   if (t_mask > 64LL * p->words_per_row)
     return fail(TILEMIX_EINVAL, "%s: %lld key-tile groups need more than %d words per row", fn,
                 (long long)t_mask, p->words_per_row);
-  if (!p->cu_seqlens_q || !p->cu_seqlens_k || !p->cu_mtiles || !p->q || !p->q8 || !p->q_scale ||
-      !p->k8 || !p->k_scale || !p->route_words || !p->out)
+  if (!p->cu_seqlens_q || !p->cu_seqlens_k || !p->cu_mtiles || !p->q || !p->k8 || !p->k_scale ||
+      !p->route_words || !p->out)
     return fail(TILEMIX_EINVAL, "%s: a required pointer is NULL", fn);
+  if ((p->q8 == nullptr) != (p->q_scale == nullptr))
+    return fail(TILEMIX_EINVAL, "%s: q8 and q_scale are both set (quantize-once) or both NULL (fused Q quantization)", fn);
   if (p->kv_int8) {
     if (p->k || p->v)
       return fail(TILEMIX_EINVAL, "%s: kv_int8 takes K/V from k8/v8; k and v must be NULL", fn);
@@ -174,8 +176,9 @@ tilemix_status check_params(const tilemix_fwd_params* p, const char* fn) {
     if (st[i] < 0 || st[i] % 8) return fail(TILEMIX_EINVAL, "%s: fp16 strides must be multiples of 8", fn);
   }
   if (!aligned(p->q, 16) || (p->k && !aligned(p->k, 16)) || (p->v && !aligned(p->v, 16)) ||
-      !aligned(p->q8, 16) || !aligned(p->k8, 16) || (p->v8 && !aligned(p->v8, 16)) ||
-      !aligned(p->out, 16) || !aligned(p->k_scale, 4) || (p->v_scale && !aligned(p->v_scale, 4)))
+      (p->q8 && !aligned(p->q8, 16)) || !aligned(p->k8, 16) || (p->v8 && !aligned(p->v8, 16)) ||
+      !aligned(p->out, 16) || !aligned(p->k_scale, 4) || (p->v_scale && !aligned(p->v_scale, 4)) ||
+      (p->q_scale && !aligned(p->q_scale, 4)))
     return fail(TILEMIX_EINVAL, "%s: tensors must be 16-byte aligned", fn);
   return TILEMIX_OK;
 }

@@ -127,11 +127,14 @@ __global__ __launch_bounds__(NWV * 64) void decode_chunk_kernel(const DecodeArgs
   const int off = Lk - Lq;  // bottom-right causal alignment
 
   // ---- the chunk's query rows into LDS
-  for (int x = tid; x < R * C16; x += NWV * 64) {
-    const int r = x / C16, c = x % C16;
-    const int64_t tok = q_begin + r / G;
-    const int h = hk * G + r % G;
-    q8s[r][c] = *reinterpret_cast<const int4v*>(a.q8 + (tok * a.hq + h) * D + 16 * c);
+  const bool fused_q = a.q8 == nullptr;  // quantize the query rows here instead of reading q8
+  if (!fused_q) {
+    for (int x = tid; x < R * C16; x += NWV * 64) {
+      const int r = x / C16, c = x % C16;
+      const int64_t tok = q_begin + r / G;
+      const int h = hk * G + r % G;
+      q8s[r][c] = *reinterpret_cast<const int4v*>(a.q8 + (tok * a.hq + h) * D + 16 * c);
+    }
   }
   for (int x = tid; x < R * (D / 8); x += NWV * 64) {
     const int r = x / (D / 8), c = x % (D / 8);
@@ -141,12 +144,39 @@ __global__ __launch_bounds__(NWV * 64) void decode_chunk_kernel(const DecodeArgs
 #pragma unroll
     for (int e = 0; e < 8; ++e) qf[r][8 * c + e] = static_cast<float>(hv[e]);
   }
-  if (tid < R) {
+  if (!fused_q && tid < R) {
     const int64_t tok = q_begin + tid / G;
     const int h = hk * G + tid % G;
     cq[tid] = a.q_scale[static_cast<int64_t>(h) * a.total_q + tok] * a.scale_log2;
   }
   __syncthreads();
+  if (fused_q) {
+    // one wavefront per row: the same fp32 operations as the quantize-once pass
+    // (a = max|x|, inv = 127 / a and a / 127 correctly rounded, rint, clamp)
+    constexpr int EPL = D / 64;  // channels per lane
+    for (int r = w; r < R; r += NWV) {
+      float xv[EPL];
+      float am = 0.0f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        xv[e] = qf[r][EPL * lane + e];
+        am = fmaxf(am, fabsf(xv[e]));
+      }
+      am = wave_max(am);
+      const float inv = am > 0.0f ? 127.0f / am : 0.0f;
+      uint32_t packed = 0;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        float c = rintf(xv[e] * inv);
+        c = fminf(fmaxf(c, -127.0f), 127.0f);
+        packed |= static_cast<uint32_t>(static_cast<uint8_t>(static_cast<int8_t>(c))) << (8 * e);
+      }
+      if (EPL == 2) reinterpret_cast<uint16_t*>(&q8s[r][0])[lane] = static_cast<uint16_t>(packed);
+      else reinterpret_cast<uint8_t*>(&q8s[r][0])[lane] = static_cast<uint8_t>(packed);
+      if (lane == 0) cq[r] = (am > 0.0f ? am / 127.0f : 0.0f) * a.scale_log2;
+    }
+    __syncthreads();
+  }
 
   const int rr = ld_uniform(a.cu_mtiles, b);
   const const_u64* wp = (const const_u64*)(a.words) + (static_cast<int64_t>(hk) * a.total_mtiles + rr) * a.wpr;

@@ -458,6 +458,48 @@ __device__ __forceinline__ void run_iter(Wave<D, KV8>& wv, const char* vst, cons
   wv.template settle<0>(rs);
 }
 
+// Fused Q quantization (the alternative to the quantize-once pass): the two lanes of a query row
+// (hl = 0, 1) each read, from the workgroup's fp16 Q in LDS, the channels [32 ks + 16 hl, +16)
+// they feed to the INT8 MFMA, share the row's absolute maximum, and compute the same codes and
+// scale as the quantize-once pass (same fp32 operations: a = max|x|, inv = 127 / a and a / 127
+// correctly rounded, rint, clamp). Returns the scale.
+template <int D>
+__device__ __forceinline__ float quantize_q_half(const char* q16, int row, int hl, int4v (&q8f)[D / 32]) {
+  using L = Smem<D>;
+  const char* base = q16 + row * L::RB16;
+  const int f = L::f16(row);
+  half8v xv[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    xv[2 * ks] = *reinterpret_cast<const half8v*>(base + 16 * ((4 * ks + 2 * hl) ^ f));
+    xv[2 * ks + 1] = *reinterpret_cast<const half8v*>(base + 16 * ((4 * ks + 2 * hl + 1) ^ f));
+  }
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(static_cast<float>(xv[i][e])));
+  am = fmaxf(am, __shfl_xor(am, 32));  // the row's other half
+  float s = 0.0f;
+  float inv = 0.0f;
+  if (am > 0.0f) {
+    inv = 127.0f / am;
+    s = am / 127.0f;
+  }
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    int4v packed = {};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float c = rintf(static_cast<float>(xv[2 * ks + i / 8][i % 8]) * inv);
+      c = fminf(fmaxf(c, -127.0f), 127.0f);
+      packed[i / 4] |= static_cast<int>(static_cast<uint32_t>(static_cast<uint8_t>(static_cast<int8_t>(c))) << (8 * (i % 4)));
+    }
+    q8f[ks] = packed;
+  }
+  return s;
+}
+
 template <int D, bool KV8, bool DUMP>
 __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a) {
   using L = Smem<D>;
@@ -540,13 +582,13 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
   }
   wv.cq = 1e-30f;
   wv.cs = a.scale_log2;
-  if (wv.row_valid) {
+  if (wv.row_valid && a.q8 != nullptr) {  // quantize-once: codes and scale from the a1 pass
     const int64_t tq = q_begin + wv.my_q;
     const int8_t* q8p = a.q8 + (tq * a.hq + h) * D;
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) wv.q8f[ks] = *reinterpret_cast<const int4v*>(q8p + 32 * ks + 16 * hl);
     wv.cq = fmaxf(a.q_scale[static_cast<int64_t>(h) * a.total_q + tq] * a.scale_log2, 1e-30f);
-  } else {
+  } else {  // rows past the sequence; with fused quantization the codes are set after the barrier
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) wv.q8f[ks] = int4v{};
   }
@@ -587,6 +629,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
     stg.s_next(sbuf + L::SSLOT);
   }
   dma_barrier();  // also publishes the fp16 Q stores
+  if (a.q8 == nullptr && wv.row_valid)  // fused: quantize this lane's half of its query row
+    wv.cq = fmaxf(quantize_q_half<D>(q16w, ROWS_W * w + r32, hl, wv.q8f) * a.scale_log2, 1e-30f);
 
   if (wave_live && n_tiles > 0) {
     const float* scl0 = reinterpret_cast<const float*>(sbuf);

@@ -19,13 +19,16 @@ class DeviceProblem:
     stream. The route words come from tilemix_pack_route_mask of the workload's routing map, or,
     with ``route_policy``, from an on-device policy computed in the step:
     ``("topk_maxabs", fp16_per_mille)`` or ``("bernoulli", fp16_per_mille, seed)``.
-    With ``kv_int8`` the INT8 K/V cache is produced once at construction by the library's
+    With ``fused_q`` the fused kernel quantizes Q itself (q8 / q_scale passed as NULL) and the
+    quantize step covers K only. With ``kv_int8`` the INT8 K/V cache is produced once at construction by the library's
     own quantizer, and the fp16 K/V are dropped."""
 
     def __init__(self, w, device: str = "cuda", out_dtype=torch.float32, with_lse: bool = True,
-                 softmax_scale: float = 0.0, route_policy: Optional[tuple] = None):
+                 softmax_scale: float = 0.0, route_policy: Optional[tuple] = None,
+                 fused_q: bool = False):
         self.w = w
         self.route_policy = route_policy
+        self.fused_q = fused_q
         dev = torch.device(device)
         T, hq, hk, d = w.total, w.hq, w.hk, w.d
         self.q = torch.from_numpy(w.q).to(dev)
@@ -64,11 +67,11 @@ class DeviceProblem:
             self.v8 = self.v_scale = None
 
     def quantize(self, stream=None):
-        if self.w.kv_int8:
-            B.tilemix_quantize_qk(q=self.q, q8=self.q8, q_scale=self.q_scale, stream=stream)
-        else:
-            B.tilemix_quantize_qk(q=self.q, q8=self.q8, q_scale=self.q_scale, k=self.k, k8=self.k8,
-                                  k_scale=self.k_scale, stream=stream)
+        qargs = {} if self.fused_q else dict(q=self.q, q8=self.q8, q_scale=self.q_scale)
+        if not self.w.kv_int8:
+            qargs.update(k=self.k, k8=self.k8, k_scale=self.k_scale)
+        if qargs:
+            B.tilemix_quantize_qk(stream=stream, **qargs)
 
     def pack(self, stream=None):
         B.tilemix_pack_route_mask(self.route.view(-1, self.route.shape[-1]),
@@ -98,7 +101,8 @@ class DeviceProblem:
                   debug_mtile_begin: int = 0, debug_mtile_count: int = 0):
         w = self.w
         B.tilemix_prefill_fwd(
-            q=self.q, k=self.k, v=self.v, q8=self.q8, q_scale=self.q_scale, k8=self.k8,
+            q=self.q, k=self.k, v=self.v, q8=None if self.fused_q else self.q8,
+            q_scale=None if self.fused_q else self.q_scale, k8=self.k8,
             k_scale=self.k_scale, v8=self.v8, v_scale=self.v_scale, route_words=self.words,
             cu_seqlens_q=self.cu, cu_seqlens_k=self.cu, cu_mtiles=self.cu_mtiles,
             max_seqlen_q=self.max_seqlen, max_seqlen_k=self.max_seqlen, route_block_m=w.bm_r,
@@ -120,11 +124,14 @@ class DeviceDecode:
     the packed route words and the outputs.
 
     ``step()`` is one decode step: tilemix_quantize_qk on the new query tokens, then
-    tilemix_decode_fwd against the cache, both on the current stream."""
+    tilemix_decode_fwd against the cache, both on the current stream. With ``fused_q`` the
+    decode kernel quantizes the new tokens itself and the step is the decode call alone."""
 
-    def __init__(self, w, device: str = "cuda", out_dtype=torch.float16, with_lse: bool = True):
+    def __init__(self, w, device: str = "cuda", out_dtype=torch.float16, with_lse: bool = True,
+                 fused_q: bool = False):
         dev = torch.device(device)
         self.w = w
+        self.fused_q = fused_q
         hq, hk, d = w.hq, w.hk, w.d
         self.q = torch.from_numpy(w.q).to(dev)
         self.q8 = torch.empty((w.total_q, hq, d), dtype=torch.int8, device=dev)
@@ -154,12 +161,13 @@ class DeviceDecode:
         self.lse = torch.empty((hq, w.total_q), dtype=torch.float32, device=dev) if with_lse else None
 
     def quantize(self, stream=None):
-        if self.w.total_q:
+        if self.w.total_q and not self.fused_q:
             B.tilemix_quantize_qk(q=self.q, q8=self.q8, q_scale=self.q_scale, stream=stream)
 
     def decode(self, softmax_scale: float = 0.0, stream=None):
         w = self.w
-        B.tilemix_decode_fwd(q=self.q, q8=self.q8, q_scale=self.q_scale, k8=self.k8,
+        B.tilemix_decode_fwd(q=self.q, q8=None if self.fused_q else self.q8,
+                             q_scale=None if self.fused_q else self.q_scale, k8=self.k8,
                              k_scale=self.k_scale, v8=self.v8, v_scale=self.v_scale,
                              route_words=self.words, cu_seqlens_q=self.cu_q, cu_seqlens_k=self.cu_k,
                              cu_mtiles=self.cu_mtiles, max_seqlen_q=self.max_q,

@@ -94,7 +94,8 @@ BAD_CASES = [
     ("route_block_n", lambda p: setattr(p, "route_block_n", 96), B.TILEMIX_EINVAL),
     ("route_group", lambda p: setattr(p, "route_group", 0), B.TILEMIX_EINVAL),
     ("too many groups", lambda p: setattr(p, "max_seqlen_k", 128 * 65), B.TILEMIX_EINVAL),
-    ("null q8", lambda p: setattr(p, "q8", None), B.TILEMIX_EINVAL),
+    ("null q8 only", lambda p: setattr(p, "q8", None), B.TILEMIX_EINVAL),
+    ("null q_scale only", lambda p: setattr(p, "q_scale", None), B.TILEMIX_EINVAL),
     ("null out", lambda p: setattr(p, "out", None), B.TILEMIX_EINVAL),
     ("kv_int8 with fp16 k", lambda p: setattr(p, "kv_int8", 1), B.TILEMIX_EINVAL),
     ("fp16 without v", lambda p: setattr(p, "v", None), B.TILEMIX_EINVAL),
