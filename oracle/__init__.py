@@ -60,6 +60,9 @@ def lib():
         L = ctypes.CDLL(_LIB_PATH)
         L.oracle_quantize_rows.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                            ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+        L.oracle_quantize_blocks.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
         L.oracle_pack_route.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                         ctypes.c_void_p, ctypes.c_int32]
         L.oracle_prefill.argtypes = [ctypes.POINTER(Problem), ctypes.c_void_p, ctypes.c_int64,
@@ -104,6 +107,21 @@ def quantize_rows(x: np.ndarray):
     rc = lib().oracle_quantize_rows(_ptr(x), rows, d, d, _ptr(q), _ptr(s))
     if rc:
         raise ValueError("oracle_quantize_rows rejected its arguments")
+    return q, s
+
+
+def quantize_blocks(x: np.ndarray, cu_seqlens, block_rows: int):
+    """Block-wise symmetric INT8 of fp16 [T, H, d]: one scale per (block of block_rows tokens of a
+    sequence, head), repeated on each row -> (int8 [T, H, d], fp32 scale [T, H])."""
+    x = np.ascontiguousarray(x, dtype=np.float16)
+    T, H, d = x.shape
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    q = np.empty(x.shape, dtype=np.int8)
+    s = np.empty((T, H), dtype=np.float32)
+    rc = lib().oracle_quantize_blocks(_ptr(x.view(np.uint16)), T, H, d, _ptr(cu), len(cu) - 1,
+                                      block_rows, _ptr(q), _ptr(s))
+    if rc:
+        raise ValueError("oracle_quantize_blocks rejected its arguments")
     return q, s
 
 

@@ -112,6 +112,48 @@ int oracle_quantize_rows(const uint16_t* x, int64_t rows, int32_t d, int64_t row
   return 0;
 }
 
+// Block-wise symmetric INT8 quantization: the TileMix paper quantizes Q and K "blockwise" with one
+// scale per block (Section 4.3, INT8 path; quantizer psi of Section 3.2). A block is `block_rows`
+// consecutive tokens of one sequence (the last block of a sequence may be shorter; blocks never
+// straddle sequences) and one head: a = max|x| over its rows and all d channels, then the same
+// fp32 steps as the per-row quantizer with that a. x is fp16 bits [T, heads, d] contiguous, q is
+// [T, heads, d], scale is [T, heads] and every row holds its block's scale.
+int oracle_quantize_blocks(const uint16_t* x, int64_t T, int32_t heads, int32_t d,
+                           const int32_t* cu, int32_t batch, int32_t block_rows, int8_t* q,
+                           float* scale) {
+  if (!x || !q || !scale || !cu || T < 0 || heads < 1 || d < 1 || batch < 1 || block_rows < 1) return -1;
+  if (cu[0] != 0 || cu[batch] != T) return -1;
+  for (int b = 0; b < batch; ++b)
+    if (cu[b + 1] < cu[b]) return -1;
+  const double* f16 = binary16_table();
+  for (int b = 0; b < batch; ++b) {
+    for (int64_t t0 = cu[b]; t0 < cu[b + 1]; t0 += block_rows) {
+      const int64_t t1 = std::min<int64_t>(cu[b + 1], t0 + block_rows);
+      for (int h = 0; h < heads; ++h) {
+        float a = 0.0f;
+        for (int64_t t = t0; t < t1; ++t)
+          for (int c = 0; c < d; ++c) {
+            const float v = static_cast<float>(std::fabs(f16[x[(t * heads + h) * d + c]]));
+            if (v > a) a = v;
+          }
+        const float inv = a > 0.0f ? 127.0f / a : 0.0f;
+        const float delta = a > 0.0f ? a / 127.0f : 0.0f;
+        for (int64_t t = t0; t < t1; ++t) {
+          scale[t * heads + h] = delta;
+          for (int c = 0; c < d; ++c) {
+            const int64_t i = (t * heads + h) * d + c;
+            float k = std::rint(static_cast<float>(f16[x[i]]) * inv);
+            if (k > 127.0f) k = 127.0f;
+            if (k < -127.0f) k = -127.0f;
+            q[i] = static_cast<int8_t>(k);
+          }
+        }
+      }
+    }
+  }
+  return 0;
+}
+
 // Packs R [rows, t_mask] of 0/1 bytes into words [rows, wpr]: bit g_j of a row is word g_j>>6,
 // bit g_j&63. Unused high bits are zero. Returns -1 on a value other than 0/1 or a short row.
 int oracle_pack_route(const uint8_t* R, int64_t rows, int32_t t_mask, uint64_t* words,
