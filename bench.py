@@ -37,6 +37,8 @@ DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_fwd_decode128k.md")
 DECODE_SRC = os.path.join(ROOT, "mixed_precision_attention_tilemix_amd", "csrc", "decode.hip")
 ROUTE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "route_topk_gqa32k.md")
 ROUTE_SRC = os.path.join(ROOT, "mixed_precision_attention_tilemix_amd", "csrc", "route.hip")
+QUANT_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quantize_gqa32k.md")
+QUANT_SRC = os.path.join(ROOT, "mixed_precision_attention_tilemix_amd", "csrc", "quantize.hip")
 
 
 def calibration_copy():
@@ -216,6 +218,97 @@ def run_decode(args):
     print(json.dumps(result), flush=True)
 
 
+def run_quantize(args):
+    """One step = the quantize-once pass over the 32k GQA workload's Q and K (tilemix_quantize_qk,
+    per-token scales); the block-wise form (tilemix_quantize_blocks, one scale per 128-token block
+    of Q and of K) is timed beside it."""
+    import torch
+    from mixed_precision_attention_tilemix_amd import binding, workloads
+
+    binding.load()
+    w = workloads.make("gqa32k")
+    dev = torch.device("cuda")
+    T, d = w.total, w.d
+    q = torch.from_numpy(w.q).to(dev)
+    k = torch.from_numpy(w.k).to(dev)
+    cu = torch.from_numpy(w.cu_seqlens).to(dev)
+    q8 = torch.empty((T, w.hq, d), dtype=torch.int8, device=dev)
+    k8 = torch.empty((T, w.hk, d), dtype=torch.int8, device=dev)
+    qs = torch.empty((w.hq, T), dtype=torch.float32, device=dev)
+    ks = torch.empty((w.hk, T), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def per_token():
+        binding.tilemix_quantize_qk(q=q, q8=q8, q_scale=qs, k=k, k8=k8, k_scale=ks)
+
+    def blocks():
+        binding.tilemix_quantize_blocks(q, q8, qs, cu, T, 128)
+        binding.tilemix_quantize_blocks(k, k8, ks, cu, T, 128)
+
+    nbytes = T * (w.hq + w.hk) * (3 * d + 4)  # fp16 read + int8 write + fp32 scale per row
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for e0, e1 in ev:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps, float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    step_ms, call_ms = timed(per_token)
+    got_q8, got_qs = q8.cpu().numpy(), qs.cpu().numpy()
+    blk_step_ms, blk_call_ms = timed(blocks)
+    result = {
+        "metric": "quantize-once pass (per-token symmetric INT8 of Q and K): effective HBM bandwidth",
+        "value": round(nbytes / (step_ms * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16 in, int8 + fp32 scale out",
+        "data": "synthetic",
+        "config": {"workload": "quantize_gqa32k", "tokens": T, "hq": w.hq, "hkv": w.hk, "head_dim": d},
+        "quantize_qk_ms": round(call_ms, 4),
+        "quantize_blocks_128_ms": round(blk_call_ms, 4),
+        "quantize_blocks_128_gbps": round(nbytes / (blk_call_ms * 1e-3) / 1e9, 1),
+        "roofline": {
+            "kernel": "quantize_rows_kernel<128> (Q and K launches of the tilemix_quantize_qk call)",
+            "bound": "hbm",
+            "achieved": round(nbytes / (call_ms * 1e-3) / 1e9, 1),
+            "peak": PEAK_HBM,
+            "unit": "GB/s",
+            "frac": round(nbytes / (call_ms * 1e-3) / 1e9 / PEAK_HBM, 4),
+            "traffic": measured_traffic(QUANT_TRAFFIC_FILE, QUANT_SRC),
+            "bytes_per_launch": nbytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        t1 = time.perf_counter()
+        rq8, rqs = oracle.quantize_rows(w.q)
+        oracle.quantize_rows(w.k)
+        dt = time.perf_counter() - t1
+        result["cpu_baseline"] = {
+            "value": round(nbytes / dt / 1e9, 3),
+            "unit": "GB/s",
+            "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"the whole step (Q and K of {T} tokens), {dt:.2f} s",
+            "seconds": dt,
+            "parity_q_codes_equal": bool(np.array_equal(got_q8, rq8) and np.array_equal(got_qs, rqs.T)),
+        }
+    print(json.dumps(result), flush=True)
+
+
 ROUTE_WORKLOADS = {"route_gqa32k": ("gqa32k", 100)}
 
 
@@ -359,12 +452,19 @@ def run_numerics(args):
             torch.cuda.synchronize()
             out = prob.out.cpu().numpy().astype(np.float64)
             n8 = int8_pair_counts(w)
+            del prob
+            # the same point with per-block scales: one per 64-token block of Q and of K
+            prob = DeviceProblem(w, out_dtype=torch.float32, scale_blocks=(w.bm_r, w.bn_r))
+            prob.step()
+            torch.cuda.synchronize()
+            out_b = prob.out.cpu().numpy().astype(np.float64)
+            del prob
             row[f"{int(round(100 * cov))}%"] = {
                 "mean_abs_dev": float(np.abs(out - exact).mean()),
                 "max_abs_dev": float(np.abs(out - exact).max()),
+                "mean_abs_dev_block_scales": float(np.abs(out_b - exact).mean()),
                 "int8_pair_fraction": round(n8 / (w.legal_pairs() * w.hq), 4),
             }
-            del prob
         table[str(L)] = row
     last = table[str(workloads.NUMERICS_LENGTHS[-1])][f"{int(round(100 * workloads.NUMERICS_COVERAGES[-1]))}%"]
     result = {
@@ -378,7 +478,8 @@ def run_numerics(args):
         "config": {"workload": "numerics", "hq": 24, "hkv": 8, "head_dim": 128, "causal": True,
                    "route_tile": [64, 64], "group": 1, "lengths": list(workloads.NUMERICS_LENGTHS),
                    "int8_coverages": list(workloads.NUMERICS_COVERAGES),
-                   "reference": "exact causal attention of the fp16 inputs, fp64, PyTorch CPU"},
+                   "reference": "exact causal attention of the fp16 inputs, fp64, PyTorch CPU",
+                   "scales": "per token (mean_abs_dev) and per 64-token block (mean_abs_dev_block_scales)"},
         "table": table,
         "seconds": round(time.perf_counter() - t0, 1),
     }
@@ -408,6 +509,9 @@ def main():
         return
     if args.workload in ROUTE_WORKLOADS:
         run_route(args)
+        return
+    if args.workload == "quantize_gqa32k":
+        run_quantize(args)
         return
     if args.workload in _wl.DECODE_WORKLOADS:
         run_decode(args)

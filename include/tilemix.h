@@ -69,6 +69,25 @@ tilemix_status tilemix_quantize_qk(const void* q, int64_t total_q, int32_t hq,
                                    float* k_scale, int32_t head_dim, void* stream);
 
 /*
+ * tilemix_quantize_blocks - the block-wise form of the quantizer (Section 4.3: Q and K quantized
+ * "blockwise" with per-block scales; psi of Section 3.2). A block is block_rows consecutive tokens
+ * of one sequence (cu_seqlens, device [batch+1]; the last block of a sequence may be shorter,
+ * blocks never straddle sequences) and one head: a = max|x| over its rows and channels, then the
+ * per-token quantizer's steps with that a. Every row of the block receives the block's scale, so
+ * x8 [n_tok, n_head, d] and scale [n_head, n_tok] have the layouts of tilemix_quantize_qk and feed
+ * tilemix_prefill_fwd / tilemix_decode_fwd unchanged (e.g. Q blocks of route_block_m rows and K
+ * blocks of route_block_n rows: one scale per route tile row / column). block_rows = 1 gives
+ * tilemix_quantize_qk's result. x is fp16 [n_tok, n_head, d] with element strides (multiples of
+ * 8, 16-byte aligned). max_seqlen >= every sequence length.
+ * Errors: EINVAL for NULL pointers, bad strides / alignment, block_rows < 1, n_head or batch
+ * outside 1..65535; EUNSUPPORTED for head_dim other than 64/128.
+ */
+tilemix_status tilemix_quantize_blocks(const void* x, int64_t n_tok, int32_t n_head, int64_t stride_tok,
+                                       int64_t stride_head, const int32_t* cu_seqlens, int32_t batch,
+                                       int32_t max_seqlen, int32_t block_rows, int8_t* x8, float* scale,
+                                       int32_t head_dim, void* stream);
+
+/*
  * tilemix_pack_route_mask - packs a routing map into bitmask words (Section 4.2, packing and
  * lookup equations: b = sum_j R_j 2^j, R_j = (b >> j) & 1).
  *

@@ -25,7 +25,7 @@ TILEMIX_OK, TILEMIX_EINVAL, TILEMIX_EUNSUPPORTED, TILEMIX_ELAUNCH = 0, 1, 2, 3
 EXPORTED = ("tilemix_last_error", "tilemix_version", "tilemix_quantize_qk",
             "tilemix_pack_route_mask", "tilemix_prefill_workspace_size", "tilemix_prefill_fwd",
             "tilemix_decode_workspace_size", "tilemix_decode_fwd", "tilemix_route_workspace_size",
-            "tilemix_route_topk_maxabs", "tilemix_route_bernoulli")
+            "tilemix_route_topk_maxabs", "tilemix_route_bernoulli", "tilemix_quantize_blocks")
 
 
 class TilemixError(RuntimeError):
@@ -105,6 +105,8 @@ def load(path: Optional[str] = None):
     L.tilemix_quantize_qk.restype = ctypes.c_int
     L.tilemix_quantize_qk.argtypes = [vp, i64, i32, i64, i64, vp, vp,
                                       vp, i64, i32, i64, i64, vp, vp, i32, vp]
+    L.tilemix_quantize_blocks.restype = ctypes.c_int
+    L.tilemix_quantize_blocks.argtypes = [vp, i64, i32, i64, i64, vp, i32, i32, i32, vp, vp, i32, vp]
     L.tilemix_pack_route_mask.restype = ctypes.c_int
     L.tilemix_pack_route_mask.argtypes = [vp, i64, i32, vp, i32, vp]
     L.tilemix_prefill_workspace_size.restype = ctypes.c_int
@@ -171,6 +173,18 @@ def tilemix_quantize_qk(q: Optional[torch.Tensor] = None, q8: Optional[torch.Ten
         qs[0], qs[1], _ptr(q8), _ptr(q_scale),
         _ptr(k), k.shape[0] if k is not None else 0, k.shape[1] if k is not None else 0,
         ks[0], ks[1], _ptr(k8), _ptr(k_scale), d, _stream(stream)))
+
+
+def tilemix_quantize_blocks(x: torch.Tensor, x8: torch.Tensor, scale: torch.Tensor,
+                            cu_seqlens: torch.Tensor, max_seqlen: int, block_rows: int,
+                            stream=None) -> None:
+    """x fp16 [T, H, d] -> x8 int8 [T, H, d], scale fp32 [H, T] with one scale per block of
+    block_rows tokens of a sequence (repeated on each row)."""
+    st = _tok_head_strides(x)
+    _check(load().tilemix_quantize_blocks(_ptr(x), x.shape[0], x.shape[1], st[0], st[1],
+                                          _ptr(cu_seqlens), cu_seqlens.shape[0] - 1, int(max_seqlen),
+                                          int(block_rows), _ptr(x8), _ptr(scale), x.shape[2],
+                                          _stream(stream)))
 
 
 def tilemix_pack_route_mask(route: torch.Tensor, words: torch.Tensor, stream=None) -> None:

@@ -45,7 +45,8 @@ tilemix_status check_quant_group(const char* name, const void* x, int64_t n, int
   if (x == nullptr && x8 == nullptr && s == nullptr) return TILEMIX_OK;
   if (x == nullptr || x8 == nullptr || s == nullptr)
     return fail(TILEMIX_EINVAL, "quantize_qk: %s input and both outputs must be all set or all NULL", name);
-  if (n < 0 || h < 1) return fail(TILEMIX_EINVAL, "quantize_qk: %s has n_tok=%lld heads=%d", name, (long long)n, h);
+  if (n < 0 || h < 1 || h > 65535)
+    return fail(TILEMIX_EINVAL, "quantize_qk: %s has n_tok=%lld heads=%d (heads 1 .. 65535)", name, (long long)n, h);
   if (st_tok < 0 || st_head < 0 || st_tok % 8 || st_head % 8)
     return fail(TILEMIX_EINVAL, "quantize_qk: %s strides must be non-negative multiples of 8 elements", name);
   if (!aligned(x, 16) || !aligned(x8, 8) || !aligned(s, 4))
@@ -272,6 +273,27 @@ tilemix_status tilemix_quantize_qk(const void* q, int64_t total_q, int32_t hq,
     if (e != hipSuccess) return from_hip(e, "quantize_qk(k)");
   }
   return ok();
+}
+
+tilemix_status tilemix_quantize_blocks(const void* x, int64_t n_tok, int32_t n_head, int64_t stride_tok,
+                                       int64_t stride_head, const int32_t* cu_seqlens, int32_t batch,
+                                       int32_t max_seqlen, int32_t block_rows, int8_t* x8, float* scale,
+                                       int32_t head_dim, void* stream) {
+  if (head_dim != 64 && head_dim != 128)
+    return fail(TILEMIX_EUNSUPPORTED, "quantize_blocks: head_dim %d (supported: 64, 128)", head_dim);
+  if (n_tok < 0 || n_head < 1 || n_head > 65535 || batch < 1 || batch > 65535 || max_seqlen < 0)
+    return fail(TILEMIX_EINVAL, "quantize_blocks: n_tok=%lld n_head=%d batch=%d max_seqlen=%d",
+                (long long)n_tok, n_head, batch, max_seqlen);
+  if (block_rows < 1) return fail(TILEMIX_EINVAL, "quantize_blocks: block_rows %d < 1", block_rows);
+  if (!x || !x8 || !scale || !cu_seqlens) return fail(TILEMIX_EINVAL, "quantize_blocks: NULL pointer");
+  if (stride_tok < 0 || stride_head < 0 || stride_tok % 8 || stride_head % 8)
+    return fail(TILEMIX_EINVAL, "quantize_blocks: strides must be non-negative multiples of 8 elements");
+  if (!aligned(x, 16) || !aligned(x8, 8) || !aligned(scale, 4))
+    return fail(TILEMIX_EINVAL, "quantize_blocks: pointers misaligned (need 16/8/4 bytes)");
+  return from_hip(tilemix::launch_quantize_blocks(x, n_tok, n_head, stride_tok, stride_head, cu_seqlens, batch,
+                                                  max_seqlen, block_rows, x8, scale, head_dim,
+                                                  static_cast<hipStream_t>(stream)),
+                  "quantize_blocks");
 }
 
 tilemix_status tilemix_pack_route_mask(const uint8_t* route, int64_t rows, int32_t t_mask,

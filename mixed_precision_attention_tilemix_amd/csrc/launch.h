@@ -11,6 +11,13 @@ hipError_t launch_quantize(const void* x, int64_t n_tok, int32_t n_head, int64_t
                            int64_t stride_head, int8_t* x8, float* scale, int32_t head_dim,
                            hipStream_t stream);
 
+// Block-wise variant: one scale per block of block_rows tokens of one sequence and head, written
+// to every row of the block ([n_head, n_tok] layout as above).
+hipError_t launch_quantize_blocks(const void* x, int64_t n_tok, int32_t n_head, int64_t stride_tok,
+                                  int64_t stride_head, const int32_t* cu, int32_t batch,
+                                  int32_t max_seqlen, int32_t block_rows, int8_t* x8, float* scale,
+                                  int32_t head_dim, hipStream_t stream);
+
 hipError_t launch_pack(const uint8_t* route, int64_t rows, int32_t t_mask, uint64_t* words,
                        int32_t words_per_row, hipStream_t stream);
 

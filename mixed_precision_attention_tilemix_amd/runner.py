@@ -20,15 +20,20 @@ class DeviceProblem:
     with ``route_policy``, from an on-device policy computed in the step:
     ``("topk_maxabs", fp16_per_mille)`` or ``("bernoulli", fp16_per_mille, seed)``.
     With ``fused_q`` the fused kernel quantizes Q itself (q8 / q_scale passed as NULL) and the
-    quantize step covers K only. With ``kv_int8`` the INT8 K/V cache is produced once at construction by the library's
+    quantize step covers K only. With ``scale_blocks=(bq, bk)`` Q and K are quantized block-wise
+    (tilemix_quantize_blocks: one scale per bq query / bk key tokens of a sequence) instead of
+    per token; with an INT8 cache the blocks apply to the cached K. With ``kv_int8`` the INT8 K/V cache is produced once at construction by the library's
     own quantizer, and the fp16 K/V are dropped."""
 
     def __init__(self, w, device: str = "cuda", out_dtype=torch.float32, with_lse: bool = True,
                  softmax_scale: float = 0.0, route_policy: Optional[tuple] = None,
-                 fused_q: bool = False):
+                 fused_q: bool = False, scale_blocks: Optional[tuple] = None):
+        if fused_q and scale_blocks is not None:
+            raise ValueError("fused Q quantization is per token; it does not take scale blocks")
         self.w = w
         self.route_policy = route_policy
         self.fused_q = fused_q
+        self.scale_blocks = scale_blocks
         dev = torch.device(device)
         T, hq, hk, d = w.total, w.hq, w.hk, w.d
         self.q = torch.from_numpy(w.q).to(dev)
@@ -59,6 +64,9 @@ class DeviceProblem:
             self.v_scale = torch.empty((hk, T), dtype=torch.float32, device=dev)
             B.tilemix_quantize_qk(q=v, q8=self.v8, q_scale=self.v_scale, k=k, k8=self.k8,
                                   k_scale=self.k_scale)
+            if scale_blocks is not None:
+                B.tilemix_quantize_blocks(k, self.k8, self.k_scale, self.cu, self.max_seqlen,
+                                          scale_blocks[1])
             del k, v
             self.k = self.v = None
         else:
@@ -67,6 +75,14 @@ class DeviceProblem:
             self.v8 = self.v_scale = None
 
     def quantize(self, stream=None):
+        if self.scale_blocks is not None:
+            bq, bk = self.scale_blocks
+            B.tilemix_quantize_blocks(self.q, self.q8, self.q_scale, self.cu, self.max_seqlen, bq,
+                                      stream=stream)
+            if not self.w.kv_int8:
+                B.tilemix_quantize_blocks(self.k, self.k8, self.k_scale, self.cu, self.max_seqlen, bk,
+                                          stream=stream)
+            return
         qargs = {} if self.fused_q else dict(q=self.q, q8=self.q8, q_scale=self.q_scale)
         if not self.w.kv_int8:
             qargs.update(k=self.k, k8=self.k8, k_scale=self.k_scale)

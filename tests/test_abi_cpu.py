@@ -334,3 +334,30 @@ def test_route_null_params_and_workspace_size(lib):
     p.route_group = 0
     assert lib.tilemix_route_workspace_size(ctypes.byref(p), ctypes.byref(n)) == B.TILEMIX_EINVAL
     assert lib.tilemix_route_workspace_size(None, ctypes.byref(n)) == B.TILEMIX_EINVAL
+
+
+QB_BAD = [
+    ("head_dim", dict(head_dim=96), B.TILEMIX_EUNSUPPORTED),
+    ("block_rows", dict(block_rows=0), B.TILEMIX_EINVAL),
+    ("n_head", dict(n_head=0), B.TILEMIX_EINVAL),
+    ("batch", dict(batch=0), B.TILEMIX_EINVAL),
+    ("negative tokens", dict(n_tok=-1), B.TILEMIX_EINVAL),
+    ("null x", dict(x=None), B.TILEMIX_EINVAL),
+    ("null cu", dict(cu=None), B.TILEMIX_EINVAL),
+    ("null scale", dict(scale=None), B.TILEMIX_EINVAL),
+    ("odd stride", dict(stride_tok=100), B.TILEMIX_EINVAL),
+    ("misaligned x", dict(x=FAKE + 8), B.TILEMIX_EINVAL),
+    ("misaligned x8", dict(x8=FAKE + 4), B.TILEMIX_EINVAL),
+]
+
+
+@pytest.mark.parametrize("name,change,status", QB_BAD, ids=[c[0] for c in QB_BAD])
+def test_quantize_blocks_validation(lib, name, change, status):
+    a = dict(x=FAKE, n_tok=1000, n_head=4, stride_tok=512, stride_head=128, cu=FAKE, batch=2,
+             max_seqlen=600, block_rows=64, x8=FAKE, scale=FAKE, head_dim=128)
+    a.update(change)
+    got = lib.tilemix_quantize_blocks(a["x"], a["n_tok"], a["n_head"], a["stride_tok"], a["stride_head"],
+                                      a["cu"], a["batch"], a["max_seqlen"], a["block_rows"], a["x8"],
+                                      a["scale"], a["head_dim"], None)
+    assert got == status, (name, B.last_error())
+    assert B.last_error().startswith("quantize_blocks")
