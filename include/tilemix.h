@@ -215,13 +215,14 @@ tilemix_status tilemix_decode_workspace_size(const tilemix_fwd_params* params, i
  * set), max_seqlen_q <= 8 and (hq / hkv) * max_seqlen_q <= 16 (EUNSUPPORTED otherwise),
  * debug_s32 NULL (EINVAL), and a workspace of tilemix_decode_workspace_size() bytes,
  * 256-byte aligned, owned by the caller (its contents on entry are irrelevant; calls that share
- * it must not overlap in time). Scores, softmax and P.V are fp32 (P is not rounded to fp16);
- * V_j = v_scale[j] * v8_j exactly.
+ * it must not overlap in time). Scores and the softmax state are fp32; P.V takes
+ * fp16(P_j * v_scale[j]) against the exact fp16 of v8_j with fp32 accumulation (as the prefill
+ * path rounds P to fp16).
  *
- * Implementation: a split-key pass (256 keys of one sequence and KV head per workgroup, every
- * query row of that KV head's GQA group) writes per-chunk max / sum / unnormalised output into
- * the workspace; a merge pass combines them into O and LSE. Both are enqueued on `stream`;
- * the result is bitwise deterministic.
+ * Implementation: a split-key pass (1024 keys of one sequence and KV head per workgroup, every
+ * query row of that KV head's GQA group, scores and P.V on the matrix cores) writes per-chunk
+ * max / sum / unnormalised output into the workspace; a merge pass combines them into O and LSE.
+ * Both are enqueued on `stream`; the result is bitwise deterministic.
  */
 tilemix_status tilemix_decode_fwd(const tilemix_fwd_params* params, void* stream);
 

@@ -2,25 +2,25 @@
 // the INT8 cache interface serves decode; Section 4.3 routed-score equation; Section 3.1
 // softmax), for gfx950.
 //
-// The work is HBM-bound (each cached key and value is read once per KV head), so it runs on the
-// vector ALUs with coalesced 16-byte loads rather than on the matrix cores:
-//
 //   decode_chunk_kernel  one workgroup per (chunk of kDecodeChunk keys, KV head, sequence) and all
 //                        query rows r = i * G + g of that KV head (G query heads of the GQA group,
-//                        L_q query tokens). Thread t scores key j0 + t against every row: the
-//                        INT8 route with 4-way int8 dot products of q8 and k8 (exact int32), the
-//                        FP16 route with fp32 products of the fp16 query and the exact integer
-//                        key; then a block-wide max / exp2 / sum per row, and P.V with 8-byte V8
-//                        loads (16 lanes per cached row). It writes per row the chunk's max m (log2
-//                        units), its sum l and its unnormalised O into the workspace.
+//                        L_q <= 8 query tokens, at most 16 rows). Each wavefront streams its own
+//                        32-key tiles through the matrix cores with the rows padded to 32: the
+//                        INT8 route scores with 32x32x32 int8 MFMAs of k8 against q8 (exact
+//                        int32), the FP16 route with 32x32x16 fp16 MFMAs of the exact fp16 key
+//                        codes against the fp16 query (fp32 accumulation); an online softmax per
+//                        row in registers; and P.V as 32x32x16 fp16 MFMAs of V^T, read from the
+//                        wavefront's LDS copy of the V8 tile with transposing reads and converted
+//                        exactly to fp16, against fp16(P * v_scale). It writes per row the chunk's
+//                        max m (log2 units), its sum l and its unnormalised O into the workspace.
 //   decode_merge_kernel  one workgroup per (row, KV head, sequence): combines the chunks,
 //                        O = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c with M = max_c m_c,
 //                        and writes O and the natural-log LSE.
 //
 // Route bits come from the same packed words as the prefill path; a decode step has L_q <= 8 query
 // tokens, fewer than a route tile's rows, so every row of a sequence reads route row
-// cu_mtiles[b], and the 64 keys of a wavefront lie in one key tile: the INT8 / FP16 choice is
-// uniform per wavefront.
+// cu_mtiles[b], and the 32 keys of a tile lie in one key tile: the INT8 / FP16 choice is uniform
+// per wavefront.
 #include "device_types.h"
 #include "launch.h"
 
@@ -30,9 +30,10 @@ namespace {
 constexpr int CH = kDecodeChunk;      // keys per chunk workgroup
 constexpr int MAXR = kDecodeMaxRows;  // query rows per (sequence, KV head)
 constexpr int NWV = 4;                // wavefronts per chunk workgroup
-constexpr int SL = 64;                // keys per wavefront slice (one per lane)
-constexpr int NSL = CH / (NWV * SL);  // slices per wavefront
-static_assert(NSL * NWV * SL == CH, "a chunk is a whole number of slices per wavefront");
+constexpr int TK = 32;                // keys per tile: the key side of one 32x32 score tile
+constexpr int NT = CH / (NWV * TK);   // tiles per wavefront
+static_assert(NT * NWV * TK == CH, "a chunk is a whole number of tiles per wavefront");
+static_assert(MAXR <= 32, "the query rows fit the 32-column side of the score tile");
 
 typedef const __attribute__((address_space(4))) uint64_t const_u64;
 typedef const __attribute__((address_space(4))) int32_t const_i32;
@@ -40,7 +41,7 @@ typedef const __attribute__((address_space(4))) int32_t const_i32;
 // Sequence offsets and route words are uniform per workgroup: scalar loads.
 __device__ __forceinline__ int ld_uniform(const int32_t* p, int i) { return ((const const_i32*)p)[i]; }
 
-// Wave-wide max / sum by DPP steps (within quads, 8 and 16 lanes, then row broadcasts that
+// Wave-wide max (or sum) by DPP steps (within quads, 8 and 16 lanes, then row broadcasts that
 // leave the total in lane 63), read back as a uniform value. Lanes a DPP step does not write
 // keep the identity of the operation.
 template <bool MAX, int CTRL, int ROW_MASK>
@@ -63,50 +64,71 @@ __device__ __forceinline__ float wave_reduce(float v) {
 }
 
 __device__ __forceinline__ float wave_max(float v) { return wave_reduce<true>(v); }
-__device__ __forceinline__ float wave_sum(float v) { return wave_reduce<false>(v); }
 
-// Signed byte e (0..3) of a 32-bit word as an exact fp32 value.
-__device__ __forceinline__ float sbyte(int x, int e) {
-  return static_cast<float>(static_cast<int8_t>(static_cast<uint32_t>(x) >> (8 * e)));
-}
+// The key row a lane feeds to the score MFMA: lane n of a 32-lane half supplies M-row n, and
+// with the rows permuted so (bits 2 and 3 of n swapped), score t of lane (row, half hl) belongs to
+// key 16 (t >> 3) + 8 hl + (t & 7) of the tile, the layout the P.V MFMA takes P in.
+__device__ __forceinline__ int perm32(int r) { return (r & 0x13) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-// Bytes of one cached int8 row pair (this lane's key row, 16-byte loads) and its scale.
-template <int D>
-__device__ __forceinline__ void load_key(const FwdArgs& a, int64_t row, int tok, int hk, int4v (&kk)[D / 16],
-                                         float& ksc) {
+// Eight signed bytes to fp16, exactly: each byte + 128 becomes the low byte of the fp16 number
+// 1024 + (byte + 128) (high byte 0x64, by a byte permute), and 1152 is subtracted.
+__device__ __forceinline__ half8v i8x8_to_f16(int2v v) {
+  half8v r;
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) kk[c] = *reinterpret_cast<const int4v*>(a.k8 + row * D + 16 * c);
-  ksc = a.k_scale[static_cast<int64_t>(hk) * a.total_k + tok];
-}
-
-// The 8-byte V8 pieces of one slice a P.V lane needs: cached rows j, j + KL, ... (clamped to the
-// last key, whose P is 0 past the end), channels 8 * cg .. 8 * cg + 7.
-template <int D, int KL>
-__device__ __forceinline__ void load_vrows(const FwdArgs& a, int k_begin, int Lk, int j, int hk, int cg,
-                                           int2v (&v)[SL / KL]) {
-#pragma unroll
-  for (int t = 0; t < SL / KL; ++t) {
-    const int jv = min(j + KL * t, Lk - 1);
-    v[t] = *reinterpret_cast<const int2v*>(a.v8 + ((static_cast<int64_t>(k_begin) + jv) * a.hkv + hk) * D + 8 * cg);
+  for (int w = 0; w < 2; ++w) {
+    const uint32_t x = static_cast<uint32_t>(v[w]) ^ 0x80808080u;
+    const half2v bias = {static_cast<_Float16>(1152.0f), static_cast<_Float16>(1152.0f)};
+    const half2v lo = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, x, 0x04010400u)) - bias;
+    const half2v hi = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u)) - bias;
+    r[4 * w] = lo[0];
+    r[4 * w + 1] = lo[1];
+    r[4 * w + 2] = hi[0];
+    r[4 * w + 3] = hi[1];
   }
+  return r;
+}
+
+typedef __attribute__((address_space(3))) int2v lds_int2v;
+
+// The global loads of one 32-key tile: this lane's key row (perm32) as the INT8 score operand,
+// 16 bytes per 32-byte k-step, its share of the V8 rows (16-byte chunks), and one per-key scale
+// (lanes 0-31: k_scale of key jt + lane, lanes 32-63: v_scale of key jt + lane - 32), for the
+// cached keys jt .. jt + 31 clamped to the last key (their scores are masked).
+template <int D>
+__device__ __forceinline__ void load_tile(const FwdArgs& a, int64_t k_begin, int Lk, int jt, int hk, int kr,
+                                          int hl, int lane, int4v (&kf)[D / 32], int4v (&vr)[TK * D / 16 / 64],
+                                          float& sc) {
+  const int8_t* krow = a.k8 + ((k_begin + min(jt + kr, Lk - 1)) * a.hkv + hk) * D;
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) kf[ks] = *reinterpret_cast<const int4v*>(krow + 32 * ks + 16 * hl);
+  constexpr int C16 = D / 16;
+#pragma unroll
+  for (int u = 0; u < TK * C16 / 64; ++u) {
+    const int c = lane + 64 * u;
+    const int key = min(jt + c / C16, Lk - 1);
+    vr[u] = *reinterpret_cast<const int4v*>(a.v8 + ((k_begin + key) * a.hkv + hk) * D + 16 * (c % C16));
+  }
+  const float* scales = hl ? a.v_scale : a.k_scale;
+  sc = scales[static_cast<int64_t>(hk) * a.total_k + k_begin + min(jt + (lane & 31), Lk - 1)];
 }
 
 // One workgroup = one chunk of CH keys of one (sequence, KV head); each wavefront streams its own
-// NSL slices of SL keys with an online softmax per query row (the next slice's key rows are
-// loaded while the current slice is scored), and the wavefronts' states are combined at the end.
-// RB bounds the query rows (G * L_q).
-template <int D, int RB>
-__global__ __launch_bounds__(NWV * 64) void decode_chunk_kernel(const DecodeArgs da) {
+// NT tiles of TK keys with an online softmax per query row (the next tile's key and value rows are
+// loaded while the current one is computed), and the wavefronts' states are combined at the end.
+template <int D>
+__global__ __launch_bounds__(NWV * 64, 2) void decode_chunk_kernel(const DecodeArgs da) {
   const FwdArgs& a = da.f;
-  constexpr int C16 = D / 16;  // 16-byte chunks of an int8 row
-  constexpr int CG = D / 8;    // P.V: channel groups of 8 per cached row
-  constexpr int KL = 64 / CG;  // P.V: cached rows a wavefront covers per step
-  __shared__ int4v q8s[RB][C16];        // int8 query rows
-  __shared__ float qf[RB][D];           // the same rows in fp16, widened (FP16 route)
-  __shared__ float cq[RB];              // q_scale * softmax_scale * log2(e) per row
-  __shared__ float pvs[NWV][SL][RB];    // per wavefront: P * v_scale of the current slice
-  __shared__ float wm[NWV][RB], wl[NWV][RB];  // per wavefront: final max and sum per row
-  __shared__ float opart[NWV][RB][D];   // per wavefront: P.V sums
+  constexpr int C16 = D / 16;          // 16-byte chunks of an int8 row
+  constexpr int KS = D / 32;           // k-steps of the INT8 score MFMA
+  constexpr int VR = D + 16;           // bytes per LDS row of a V8 tile (padded: no bank conflicts)
+  constexpr int VU = TK * C16 / 64;    // 16-byte V8 chunks per lane per tile
+  __shared__ int4v q8s[MAXR][C16];                             // int8 query rows
+  __shared__ __attribute__((aligned(16))) _Float16 qh[MAXR][D];  // fp16 query rows (FP16 route)
+  __shared__ float cq[MAXR];                                   // q_scale * softmax_scale * log2(e)
+  __shared__ __attribute__((aligned(16))) int8_t vt8[NWV][TK * VR];  // per wavefront: V8 tile
+  __shared__ __attribute__((aligned(16))) float tsc[NWV][2 * TK];    // per wavefront: k_scale, v_scale
+  __shared__ float wm[NWV][MAXR], wl[NWV][MAXR];               // per wavefront: max and sum per row
+  __shared__ float opart[NWV][MAXR][D];                        // per wavefront: P.V sums
 
   const int chunk = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -114,8 +136,8 @@ __global__ __launch_bounds__(NWV * 64) void decode_chunk_kernel(const DecodeArgs
   const int G = a.hq / a.hkv;
   const int q_begin = ld_uniform(a.cu_q, b);
   const int Lq = ld_uniform(a.cu_q, b + 1) - q_begin;
-  const int k_begin = ld_uniform(a.cu_k, b);
-  const int Lk = ld_uniform(a.cu_k, b + 1) - k_begin;
+  const int64_t k_begin = ld_uniform(a.cu_k, b);
+  const int Lk = ld_uniform(a.cu_k, b + 1) - static_cast<int>(k_begin);
   const int R = G * Lq;
   const int j0 = chunk * CH;
   float* part = da.part + ((static_cast<int64_t>(b) * a.hkv + hk) * da.nchunk + chunk) * da.rmax * (D + 4);
@@ -140,9 +162,8 @@ __global__ __launch_bounds__(NWV * 64) void decode_chunk_kernel(const DecodeArgs
     const int r = x / (D / 8), c = x % (D / 8);
     const int64_t tok = q_begin + r / G;
     const int h = hk * G + r % G;
-    const half8v hv = *reinterpret_cast<const half8v*>(a.q + tok * a.q_stride_tok + h * a.q_stride_head + 8 * c);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qf[r][8 * c + e] = static_cast<float>(hv[e]);
+    *reinterpret_cast<half8v*>(&qh[r][8 * c]) =
+        *reinterpret_cast<const half8v*>(a.q + tok * a.q_stride_tok + h * a.q_stride_head + 8 * c);
   }
   if (!fused_q && tid < R) {
     const int64_t tok = q_begin + tid / G;
@@ -159,7 +180,7 @@ __global__ __launch_bounds__(NWV * 64) void decode_chunk_kernel(const DecodeArgs
       float am = 0.0f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
-        xv[e] = qf[r][EPL * lane + e];
+        xv[e] = static_cast<float>(qh[r][EPL * lane + e]);
         am = fmaxf(am, fabsf(xv[e]));
       }
       am = wave_max(am);
@@ -180,151 +201,150 @@ __global__ __launch_bounds__(NWV * 64) void decode_chunk_kernel(const DecodeArgs
 
   const int rr = ld_uniform(a.cu_mtiles, b);
   const const_u64* wp = (const const_u64*)(a.words) + (static_cast<int64_t>(hk) * a.total_mtiles + rr) * a.wpr;
-  const int cg = lane % CG, kq = lane / CG;  // P.V lane = (cached row kq, channel group cg)
-  const int jw0 = j0 + NSL * SL * w;         // first key of this wavefront's slices
 
-  float m[RB], l[RB], acc[RB][8];
+  // this lane: query row r32 of the padded 32 (real iff r32 < R), key half hl of each 16-key step
+  const int r32 = lane & 31, hl = lane >> 5;
+  const bool row_valid = r32 < R;
+  const int lim = !row_valid ? -1 : (a.causal ? min(Lk - 1, r32 / G + off) : Lk - 1);
+  int4v qb[KS];  // the INT8 score operand of this lane's row
 #pragma unroll
-  for (int r = 0; r < RB; ++r) {
-    m[r] = -INFINITY;
-    l[r] = 0.0f;
+  for (int ks = 0; ks < KS; ++ks) qb[ks] = row_valid ? q8s[r32][2 * ks + hl] : int4v{};
+  const float cqr = row_valid ? cq[r32] : 0.0f;
+  const float csr = row_valid ? a.scale_log2 : 0.0f;
+  const int kr = perm32(r32);
+  // transposing V8 reads: lane m of a 16-lane group g supplies row 8 (g >> 1) + (m >> 1), bytes
+  // 16 (g & 1) + 8 (m & 1); it receives channel (lane & 31) of the 8 keys 8 hl .. 8 hl + 7
+  const int vsrc = (8 * hl + ((lane & 15) >> 1)) * VR + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+  int8_t* const vt = vt8[w];
+  const int jw0 = j0 + NT * TK * w;  // first key of this wavefront's tiles
+
+  float16v o[D / 32];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[r][e] = 0.0f;
-  }
-  // the first slice's key rows and V rows; each slice then loads the next slice's ones
-  int4v kk[C16];
-  float ksc = 0.0f;
-  int2v vrow[SL / KL];
-  if (jw0 < Lk) {
-    const int jc = min(jw0 + lane, Lk - 1);
-    load_key<D>(a, (static_cast<int64_t>(k_begin) + jc) * a.hkv + hk, k_begin + jc, hk, kk, ksc);
-    load_vrows<D, KL>(a, k_begin, Lk, jw0 + kq, hk, cg, vrow);
-  }
+  for (int i = 0; i < D / 32; ++i) o[i] = float16v{};
+  float m = -INFINITY, l = 0.0f;
 
-  for (int sl = 0; sl < NSL; ++sl) {
-    const int js = jw0 + SL * sl;  // first key of the slice (uniform)
-    if (js >= Lk) break;
-    const int j = js + lane;
-    const int jc = min(j, Lk - 1);
-    const float vsc = a.v_scale[static_cast<int64_t>(hk) * a.total_k + k_begin + jc];
-    // the next slice's key rows and V rows
-    int4v kn[C16];
-    float ksn = 0.0f;
-    int2v vn[SL / KL];
-    const bool more = sl + 1 < NSL && js + SL < Lk;
-    if (more) {
-      const int jn = min(js + SL + lane, Lk - 1);
-      load_key<D>(a, (static_cast<int64_t>(k_begin) + jn) * a.hkv + hk, k_begin + jn, hk, kn, ksn);
-      load_vrows<D, KL>(a, k_begin, Lk, js + SL + kq, hk, cg, vn);
-    }
+  int4v kf[KS], vr[VU];
+  float scl = 0.0f;
+  if (jw0 < Lk) load_tile<D>(a, k_begin, Lk, jw0, hk, kr, hl, lane, kf, vr, scl);
+  float* const ts = tsc[w];
 
-    // scores (log2 units) of key j against every row, by the slice's route bit
-    const int gj = (js / a.bn_r) / a.group;
+  for (int t = 0; t < NT; ++t) {
+    const int jt = jw0 + TK * t;  // first key of the tile (uniform)
+    if (jt >= Lk) break;
+    int4v kn[KS], vn[VU];
+    float scn = 0.0f;
+    const bool more = t + 1 < NT && jt + TK < Lk;
+    if (more) load_tile<D>(a, k_begin, Lk, jt + TK, hk, kr, hl, lane, kn, vn, scn);
+    ts[lane] = scl;  // this tile's k_scale / v_scale, read back below by the lanes that need them
+
+    // scores of the tile: lane (r32, hl) gets row r32 against keys jt + 16 (e >> 3) + 8 hl + (e & 7)
+    const int gj = (jt / a.bn_r) / a.group;
     const bool i8 = ((wp[gj >> 6] >> (gj & 63)) & 1u) != 0u;
-    float sc[RB];
+    float16v sc;
+    float rowf;
     if (i8) {
+      int16v acc = {};
 #pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        if (r < R) {
-          int dot = 0;
+      for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[ks], qb[ks], acc, 0, 0, 0);
 #pragma unroll
-          for (int c = 0; c < C16; ++c) {
-            const int4v qv = q8s[r][c];
+      for (int e = 0; e < 16; ++e) sc[e] = static_cast<float>(acc[e]);
+      rowf = cqr;
+    } else {
+      // the fp16 operand wants key bytes [16 s + 8 hl, +8) per 16-byte step s; this lane holds
+      // [32 ks + 16 hl, +16) and swaps the missing 8 bytes with the other half of the wave
+      float16v acc = {};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dot = __builtin_amdgcn_sdot4(qv[e], kk[c][e], dot, false);
-          }
-          sc[r] = static_cast<float>(dot) * (cq[r] * ksc);
+      for (int ks = 0; ks < KS; ++ks) {
+        const int2v mine_lo = {kf[ks][0], kf[ks][1]}, mine_hi = {kf[ks][2], kf[ks][3]};
+        const int2v send = hl ? mine_lo : mine_hi;
+        const int2v recv = {__shfl_xor(send[0], 32), __shfl_xor(send[1], 32)};
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const int2v kb = s2 == 0 ? (hl ? recv : mine_lo) : (hl ? mine_hi : recv);
+          const int kc = 32 * ks + 16 * s2 + 8 * hl;
+          const half8v qv = row_valid ? *reinterpret_cast<const half8v*>(&qh[r32][kc]) : half8v{};
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(i8x8_to_f16(kb), qv, acc, 0, 0, 0);
         }
       }
-    } else {
-      float dot[RB];
+      sc = acc;
+      rowf = csr;
+    }
+    // the per-key scales of this lane's keys (two runs of 8: jt + 8 hl and jt + 16 + 8 hl)
+    asm volatile("" ::: "memory");
+    float ksc[16], vsc[16];
 #pragma unroll
-      for (int r = 0; r < RB; ++r) dot[r] = 0.0f;
+    for (int q = 0; q < 4; ++q) {
+      const int k0 = 16 * (q >> 1) + 8 * hl + 4 * (q & 1);
+      const float4v kv = *reinterpret_cast<const float4v*>(ts + k0);
+      const float4v vv = *reinterpret_cast<const float4v*>(ts + TK + k0);
 #pragma unroll
-      for (int c = 0; c < C16; ++c)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float kf[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) kf[t] = sbyte(kk[c][e], t);
-#pragma unroll
-          for (int r = 0; r < RB; ++r) {
-            if (r < R) {
-              const float4v qv = *reinterpret_cast<const float4v*>(&qf[r][16 * c + 4 * e]);
-#pragma unroll
-              for (int t = 0; t < 4; ++t) dot[r] = __builtin_fmaf(qv[t], kf[t], dot[r]);
-            }
-          }
-        }
-#pragma unroll
-      for (int r = 0; r < RB; ++r)
-        if (r < R) sc[r] = dot[r] * (a.scale_log2 * ksc);
+      for (int i = 0; i < 4; ++i) {
+        ksc[4 * q + i] = kv[i];
+        vsc[4 * q + i] = vv[i];
+      }
     }
 
-    // online softmax over this wavefront's keys; O and l are rescaled only when the max rises
+    // log2-unit scores with the per-key factor, legality mask, tile max of the row
+    float x[16];
+    float mt = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      if (r < R) {
-        const bool legal = j < Lk && (!a.causal || j <= r / G + off);
-        const float s = legal ? sc[r] : -INFINITY;
-        const float mn = fmaxf(m[r], wave_max(s));  // uniform
-        if (mn > m[r]) {
-          const float alpha = __builtin_amdgcn_exp2f(m[r] - mn);  // m = -inf: 0, and O, l are 0
-          l[r] *= alpha;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[r][e] *= alpha;
-          m[r] = mn;
-        }
-        const float p = s == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s - m[r]);
-        l[r] += wave_sum(p);
-        pvs[w][lane][r] = p * vsc;
-      }
+    for (int e = 0; e < 16; ++e) {
+      const int key = jt + 16 * (e >> 3) + 8 * hl + (e & 7);
+      x[e] = key > lim ? -INFINITY : sc[e] * (rowf * ksc[e]);
+      mt = fmaxf(mt, x[e]);
     }
-    // the slice's P is read back by other lanes of this wavefront (in-order LDS within a wave)
+    mt = fmaxf(mt, __shfl_xor(mt, 32));  // the row's other key half
+    if (__any(mt > m)) {
+      const float alpha = mt > m ? __builtin_amdgcn_exp2f(m - mt) : 1.0f;  // m = -inf: 0
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) o[i] *= alpha;
+      l *= alpha;
+      m = fmaxf(m, mt);
+    }
+    half8v ph[2];  // fp16 P * v_scale, [16-key step]
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = x[e] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x[e] - m);
+      l += p;
+      ph[e >> 3][e & 7] = static_cast<_Float16>(p * vsc[e]);
+    }
+
+    // the V8 tile into this wavefront's LDS rows, then O^T += V^T (P v_scale)^T
+#pragma unroll
+    for (int u = 0; u < VU; ++u) {
+      const int c = lane + 64 * u;
+      *reinterpret_cast<int4v*>(vt + (c / C16) * VR + 16 * (c % C16)) = vr[u];
+    }
     asm volatile("" ::: "memory");
 #pragma unroll
-    for (int t = 0; t < SL / KL; ++t) {
-      const int2v v8 = vrow[t];
-      float vf[8];
+    for (int dblk = 0; dblk < D / 32; ++dblk)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vf[e] = sbyte(v8[0], e);
-        vf[4 + e] = sbyte(v8[1], e);
+      for (int kk = 0; kk < 2; ++kk) {
+        const int2v v8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_int2v*)(vt + 16 * kk * VR + 32 * dblk + vsrc));
+        o[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(i8x8_to_f16(v8), ph[kk], o[dblk], 0, 0, 0);
       }
-#pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        if (r < R) {
-          const float p = pvs[w][kq + KL * t][r];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[r][e] = __builtin_fmaf(p, vf[e], acc[r][e]);
-        }
-      }
-    }
     asm volatile("" ::: "memory");
     if (more) {
 #pragma unroll
-      for (int c = 0; c < C16; ++c) kk[c] = kn[c];
+      for (int ks = 0; ks < KS; ++ks) kf[ks] = kn[ks];
 #pragma unroll
-      for (int t = 0; t < SL / KL; ++t) vrow[t] = vn[t];
-      ksc = ksn;
+      for (int u = 0; u < VU; ++u) vr[u] = vn[u];
+      scl = scn;
     }
   }
 
-  // this wavefront's state: sums over the cached rows kq of a channel group, then into LDS
+  // this wavefront's state into LDS: lane (r32, hl) holds channels 32 dblk + 8 g + 4 hl + e
+  const float l_row = l + __shfl_xor(l, 32);
+  if (row_valid) {
 #pragma unroll
-  for (int r = 0; r < RB; ++r) {
-    if (r < R) {
+    for (int dblk = 0; dblk < D / 32; ++dblk)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float v = acc[r][e];
+      for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int o = CG; o < 64; o <<= 1) v += __shfl_xor(v, o);
-        if (kq == 0) opart[w][r][8 * cg + e] = v;
-      }
-      if (lane == 0) {
-        wm[w][r] = m[r];
-        wl[w][r] = l[r];
-      }
+        for (int e = 0; e < 4; ++e) opart[w][r32][32 * dblk + 8 * g + 4 * hl + e] = o[dblk][4 * g + e];
+    if (hl == 0) {
+      wm[w][r32] = m;
+      wl[w][r32] = l_row;
     }
   }
   __syncthreads();
@@ -334,13 +354,13 @@ __global__ __launch_bounds__(NWV * 64) void decode_chunk_kernel(const DecodeArgs
     float M = wm[0][r];
 #pragma unroll
     for (int i = 1; i < NWV; ++i) M = fmaxf(M, wm[i][r]);
-    float o = 0.0f;
+    float ov = 0.0f;
     if (M > -INFINITY) {
 #pragma unroll
       for (int i = 0; i < NWV; ++i)
-        if (wm[i][r] > -INFINITY) o += __builtin_amdgcn_exp2f(wm[i][r] - M) * opart[i][r][c];
+        if (wm[i][r] > -INFINITY) ov += __builtin_amdgcn_exp2f(wm[i][r] - M) * opart[i][r][c];
     }
-    part[r * (D + 4) + 4 + c] = o;
+    part[r * (D + 4) + 4 + c] = ov;
   }
   if (tid < R) {
     float M = wm[0][tid];
@@ -431,12 +451,7 @@ hipError_t launch_t(const DecodeArgs& a, int32_t batch, hipStream_t stream) {
   if (a.rmax == 0 || batch == 0) return hipSuccess;
   if (a.nchunk > 0) {
     dim3 grid(static_cast<unsigned>(a.nchunk), static_cast<unsigned>(a.f.hkv), static_cast<unsigned>(batch));
-    if (a.rmax <= 4)
-      decode_chunk_kernel<D, 4><<<grid, dim3(NWV * 64), 0, stream>>>(a);
-    else if (a.rmax <= 8)
-      decode_chunk_kernel<D, 8><<<grid, dim3(NWV * 64), 0, stream>>>(a);
-    else
-      decode_chunk_kernel<D, MAXR><<<grid, dim3(NWV * 64), 0, stream>>>(a);
+    decode_chunk_kernel<D><<<grid, dim3(NWV * 64), 0, stream>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
