@@ -223,9 +223,11 @@ __global__ __launch_bounds__(NWV * 64, 2) void decode_chunk_kernel(const DecodeA
   for (int i = 0; i < D / 32; ++i) o[i] = float16v{};
   float m = -INFINITY, l = 0.0f;
 
+  // the loads are issued unconditionally (their keys are clamped to the sequence), so every
+  // path through the loop has the same loads in flight and each wait covers only older ones
   int4v kf[KS], vr[VU];
   float scl = 0.0f;
-  if (jw0 < Lk) load_tile<D>(a, k_begin, Lk, jw0, hk, kr, hl, lane, kf, vr, scl);
+  load_tile<D>(a, k_begin, Lk, jw0, hk, kr, hl, lane, kf, vr, scl);
   float* const ts = tsc[w];
 
   for (int t = 0; t < NT; ++t) {
@@ -233,8 +235,9 @@ __global__ __launch_bounds__(NWV * 64, 2) void decode_chunk_kernel(const DecodeA
     if (jt >= Lk) break;
     int4v kn[KS], vn[VU];
     float scn = 0.0f;
-    const bool more = t + 1 < NT && jt + TK < Lk;
-    if (more) load_tile<D>(a, k_begin, Lk, jt + TK, hk, kr, hl, lane, kn, vn, scn);
+    // past the wavefront's last tile the prefetch re-reads the current one (a cache hit) rather
+    // than the next wavefront's first tile
+    load_tile<D>(a, k_begin, Lk, min(jt + TK, jw0 + (NT - 1) * TK), hk, kr, hl, lane, kn, vn, scn);
     ts[lane] = scl;  // this tile's k_scale / v_scale, read back below by the lanes that need them
 
     // scores of the tile: lane (r32, hl) gets row r32 against keys jt + 16 (e >> 3) + 8 hl + (e & 7)
@@ -324,13 +327,11 @@ __global__ __launch_bounds__(NWV * 64, 2) void decode_chunk_kernel(const DecodeA
         o[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(i8x8_to_f16(v8), ph[kk], o[dblk], 0, 0, 0);
       }
     asm volatile("" ::: "memory");
-    if (more) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kf[ks] = kn[ks];
+    for (int ks = 0; ks < KS; ++ks) kf[ks] = kn[ks];
 #pragma unroll
-      for (int u = 0; u < VU; ++u) vr[u] = vn[u];
-      scl = scn;
-    }
+    for (int u = 0; u < VU; ++u) vr[u] = vn[u];
+    scl = scn;
   }
 
   // this wavefront's state into LDS: lane (r32, hl) holds channels 32 dblk + 8 g + 4 hl + e
