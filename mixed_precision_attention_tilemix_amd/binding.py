@@ -94,7 +94,7 @@ def load(path: Optional[str] = None):
         return _lib
     path = path or LIB_PATH
     if not os.path.exists(path):
-        raise FileNotFoundError(f"{path} is missing: build it with __graft_entry__.build() "
+        raise FileNotFoundError(f"{path} is missing: build it with python -m mixed_precision_attention_tilemix_amd.build "
                                 "(hipcc, gfx950); there is no fallback path")
     L = ctypes.CDLL(path)
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
