@@ -195,3 +195,18 @@ class DeviceDecode:
     def step(self, stream=None):
         self.quantize(stream)
         self.decode(stream=stream)
+
+    def capture(self):
+        """Record one step into a HIP graph (torch.cuda.CUDAGraph) and return it; replaying it
+        runs the step on the current contents of the input tensors (new query tokens written into
+        ``self.q`` in place are picked up). The step's kernels clear nothing with memset, so the
+        graph holds kernel nodes only."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):  # warm-up outside the capture, as the capture API asks
+            self.step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.step()
+        return graph
