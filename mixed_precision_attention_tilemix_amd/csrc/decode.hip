@@ -13,7 +13,8 @@
 //                        wavefront's LDS copy of the V8 tile with transposing reads and converted
 //                        exactly to fp16, against fp16(P * v_scale). It writes per row the chunk's
 //                        max m (log2 units), its sum l and its unnormalised O into the workspace.
-//   decode_merge_kernel  one workgroup per (row, KV head, sequence): combines the chunks,
+//   decode_merge_kernel  one workgroup per (row, 32-channel slice, KV head, sequence): combines
+//                        the chunks,
 //                        O = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c with M = max_c m_c,
 //                        and writes O and the natural-log LSE.
 //
@@ -378,18 +379,22 @@ __global__ __launch_bounds__(NWV * 64, 2) void decode_chunk_kernel(const DecodeA
   }
 }
 
-constexpr int MG = 8;  // merge: chunk groups per workgroup
+constexpr int MQ = 8;          // merge: 4-channel quads per workgroup (a 32-channel slice)
+constexpr int MG = 256 / MQ;   // merge: chunk groups per workgroup
 
+// One workgroup per (query row, 32-channel slice, KV head, sequence): the chunks' maxima give M;
+// 32 chunk groups rescale and sum their chunks' (l, O) for the slice, and the groups are added.
 template <int D>
-__global__ __launch_bounds__(MG * D / 4) void decode_merge_kernel(const DecodeArgs da) {
+__global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeArgs da) {
   const FwdArgs& a = da.f;
-  constexpr int NT = MG * D / 4;
-  __shared__ float smax[NT / 64];
+  constexpr int NS = D / (4 * MQ);  // channel slices per row
+  __shared__ float smax[4];
   __shared__ float lpart[MG];
-  __shared__ float4v opart[MG][D / 4];
-  const int r = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  __shared__ float4v opart[MG][MQ];
+  const int r = blockIdx.x / NS, slice = blockIdx.x % NS, hk = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int cgrp = tid / (D / 4), quad = tid % (D / 4);  // chunk group, 4-channel quad
+  const int cgrp = tid / MQ, q4 = tid % MQ;  // chunk group, quad within the slice
+  const int quad = slice * MQ + q4;          // 4-channel quad of the row
   const int G = a.hq / a.hkv;
   const int q_begin = ld_uniform(a.cu_q, b);
   const int Lq = ld_uniform(a.cu_q, b + 1) - q_begin;
@@ -400,14 +405,11 @@ __global__ __launch_bounds__(MG * D / 4) void decode_merge_kernel(const DecodeAr
   const float* base = da.part + (static_cast<int64_t>(b) * a.hkv + hk) * da.nchunk * stride + r * (D + 4);
   // M = max over the chunks
   float M = -INFINITY;
-  for (int ch = tid; ch < nch; ch += NT) M = fmaxf(M, base[ch * stride]);
+  for (int ch = tid; ch < nch; ch += 256) M = fmaxf(M, base[ch * stride]);
   M = wave_max(M);
   if (lane == 0) smax[tid / 64] = M;
   __syncthreads();
-  M = smax[0];
-#pragma unroll
-  for (int i = 1; i < NT / 64; ++i) M = fmaxf(M, smax[i]);
-  // each chunk group rescales and sums its chunks, then the groups are added
+  M = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
   float L = 0.0f;
   float4v O = {0.0f, 0.0f, 0.0f, 0.0f};
   if (M > -INFINITY) {
@@ -421,8 +423,8 @@ __global__ __launch_bounds__(MG * D / 4) void decode_merge_kernel(const DecodeAr
       O += f * o4;
     }
   }
-  opart[cgrp][quad] = O;
-  if (quad == 0) lpart[cgrp] = L;
+  opart[cgrp][q4] = O;
+  if (q4 == 0) lpart[cgrp] = L;
   __syncthreads();
   if (cgrp != 0) return;
   float Lt = 0.0f;
@@ -430,7 +432,7 @@ __global__ __launch_bounds__(MG * D / 4) void decode_merge_kernel(const DecodeAr
 #pragma unroll
   for (int i = 0; i < MG; ++i) {
     Lt += lpart[i];
-    Ot += opart[i][quad];
+    Ot += opart[i][q4];
   }
   const int64_t tok = q_begin + r / G;
   const int h = hk * G + r % G;
@@ -456,8 +458,9 @@ hipError_t launch_t(const DecodeArgs& a, int32_t batch, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  dim3 grid(static_cast<unsigned>(a.rmax), static_cast<unsigned>(a.f.hkv), static_cast<unsigned>(batch));
-  decode_merge_kernel<D><<<grid, dim3(MG * D / 4), 0, stream>>>(a);
+  dim3 grid(static_cast<unsigned>(a.rmax * (D / (4 * MQ))), static_cast<unsigned>(a.f.hkv),
+            static_cast<unsigned>(batch));
+  decode_merge_kernel<D><<<grid, dim3(256), 0, stream>>>(a);
   return hipGetLastError();
 }
 
