@@ -18,25 +18,31 @@
 //   * the route bit of a key tile is uniform over each wavefront (route tiles are multiples of
 //     32 rows and 64 keys), so the FP16 / INT8 choice is a wave-uniform branch.
 //
-// Software pipeline (per wavefront, in 32-key halves h of the 64-key tiles)
-//   Each step overlaps, in one straight-line block, the softmax of half h (VALU) with the P.V
-//   of half h-1 and the score MFMAs of half h+1 (matrix cores), so one wavefront keeps both
-//   pipes busy; the second wavefront of the SIMD fills what is left. One barrier per 64-key
-//   tile; K tiles (fp16 and/or int8, as the route bits of the workgroup ask) are fetched two
-//   tiles ahead and V^T tiles one tile ahead with direct global->LDS loads.
+// Schedule (per wavefront, one 64-key tile per iteration)
+//   After the tile's barrier each wavefront issues the score MFMAs of both 32-key halves, then
+//   converts and exponentiates both (VALU) with one slow-path check for the tile, then issues
+//   both halves' P.V MFMAs; the second half's scores overlap the first half's conversion, and
+//   the other wavefront of the SIMD fills the rest. A deeper software pipeline across tiles
+//   (scores of the next tile during this tile's softmax) measured slower: its extra live
+//   registers pushed the kernel into spills. One barrier per 64-key tile; the next tile's K
+//   (fp16 and/or int8, as the route bits of the workgroup ask), V^T and per-key factors are
+//   fetched with direct global->LDS loads while the current tile is computed.
 //
 // Softmax
 //   Base 2, with the score scale folded into one FMA per element. The running max is only
-//   raised when needed: each half is exponentiated against the current max, and only if some
-//   lane's sum of P exceeds 2^15 (so that no P can overflow fp16) or the row has no max yet
-//   does the wavefront take the slow path, which takes the true max, rescales O and l and
-//   recomputes P. The row sum is taken from the fp16-rounded P that also feeds P.V and is kept
+//   raised when needed: each tile is exponentiated against the current max, and only if some
+//   lane's sum of P over the tile exceeds 2^15 (so that no P can overflow fp16) or the row has
+//   no max yet does the wavefront take the slow path, which takes the true max, rescales O and
+//   l and recomputes P. The row sum is taken from the fp16-rounded P that also feeds P.V and is kept
 //   per lane half until the epilogue.
 //
 // INT8 scores
-//   The int32 accumulator starts at the bit pattern of 1.5 * 2^23; as |q8 . k8| < 2^22 it then
-//   reads as the fp32 number 1.5 * 2^23 + q8 . k8 exactly, and one FMA with the per-key factors
-//   of the V^T pre-pass gives dk' * (q8 . k8) (see vt_pack.hip).
+//   The int32 accumulator is converted to fp32 and multiplied by the per-key factor dk' of the
+//   V^T pre-pass, then one FMA with the per-row factor and the running max gives the exponent.
+//   kBiasedI8 selects the alternative in which the accumulator starts at the bit pattern of
+//   1.5 * 2^23 (as |q8 . k8| < 2^22 it then reads as the fp32 number 1.5 * 2^23 + q8 . k8
+//   exactly, and one FMA with (dk', -1.5 * 2^23 * dk') gives dk' * (q8 . k8)); it saves the
+//   conversion but reads twice the factors and measured slower.
 #include "device_types.h"
 #include "launch.h"
 #include "tile_layout.h"
@@ -48,7 +54,7 @@ constexpr int BN = kKeyTile;  // keys per pipeline tile
 constexpr int NW = 8;         // wavefronts per workgroup
 constexpr int ROWS_W = 32;    // query rows per wavefront
 constexpr int BM = NW * ROWS_W;
-constexpr float P_LIMIT = 32768.0f;  // fast path: a lane's sum of P over a half stays below this
+constexpr float P_LIMIT = 32768.0f;  // fast path: a lane's sum of P over a tile stays below this
 constexpr int I8_BIAS = 0x4B400000;  // fp32 bits of 1.5 * 2^23
 // true: INT8 accumulators start at I8_BIAS and one FMA with (dk', bk) rescales them;
 // false: they start at 0 and are converted, then multiplied by dk'
@@ -70,9 +76,9 @@ struct Smem {
   static constexpr int KSTAGE = K8 + BN * RB8;
   static constexpr int VBUF = KBUF + 2 * KSTAGE;  // two V^T stages, [D][BN] fp16 as vt_pack.hip
   static constexpr int VSTAGE = D * BN * 2;
-  static constexpr int SBUF = VBUF + 2 * VSTAGE;  // three slots of per-key factors
+  static constexpr int SBUF = VBUF + 2 * VSTAGE;  // two slots of per-key factors
   static constexpr int SSLOT = 2 * BN * 4;        // dk'[BN], bk[BN]
-  static constexpr int BYTES = SBUF + 3 * SSLOT;
+  static constexpr int BYTES = SBUF + 2 * SSLOT;
   // The 16 lanes served together read 16 different rows at one chunk index: XOR-ing the chunk
   // with (row / rows-per-256-bytes) puts them on 16 distinct 16-byte bank groups.
   __device__ static int f16(int r) { return (r / (256 / RB16)) & (C16 - 1); }
@@ -232,7 +238,6 @@ __device__ __forceinline__ uint32_t group_bits(const const_u64* wrow, int wpr, i
 }
 
 // Per-wavefront registers: constants of the wave's rows and the online-softmax state.
-// Per-wavefront registers: constants of the wave's rows and the online-softmax state.
 template <int D, bool KV8>
 struct Wave {
   int hl, my_q;
@@ -257,8 +262,7 @@ struct Wave {
   // With DUMP, the raw int32 accumulators of an INT8 half also go to the debug dump when
   // dump_row is not NULL: key j of this lane's query row is dump_row[(j / bn_r) * tile_stride +
   // j % bn_r], for the keys j < Lk; key0 = sequence-local index of the half's first key.
-  // FENCED: the call sits alone between scheduling fences (the generic iteration), and the FP16
-  // chain is split by one more fence so that fewer operands are in flight.
+  // FENCED: the FP16 chain is split by a scheduling fence so that fewer operands are in flight.
   template <int KB, bool I8, bool DUMP, bool FENCED = false>
   __device__ __forceinline__ void qk(const char* kst, const char* q16, int32_t* dump_row, int key0, int Lk,
                                      int bn_r, int tile_stride) {
@@ -352,55 +356,26 @@ struct Wave {
     return rs;
   }
 
-  // This lane's sum of the fp16 P of half KB, in the order softmax() adds it.
-  template <int KB>
-  __device__ __forceinline__ float psum() const {
-    float r = 0.0f;
+  // Both halves of a tile after their softmax (P of each half against m_use): one slow-path
+  // check for the tile; the slow path raises the max over both halves and recomputes both P.
+  __device__ __forceinline__ void settle_tile(float rs0, float rs1) {
+    if (__any(row_valid && (!(rs0 + rs1 <= P_LIMIT) || m == -INFINITY))) {
+      float mx = -INFINITY;
 #pragma unroll
-    for (int g8 = 0; g8 < 2; ++g8)
+      for (int t = 0; t < 16; ++t) mx = fmaxf(mx, fmaxf(s[0][t] * c[0], s[1][t] * c[1]));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if (mx > m) {
+        const float alpha = fast_exp2(m - mx);
 #pragma unroll
-      for (int e = 0; e < 8; e += 2)
-        r = __builtin_amdgcn_fdot2(half2v{p[KB][g8][e], p[KB][g8][e + 1]},
-                                   half2v{static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)}, r, false);
-    return r;
-  }
-
-  // Slow path of half KB: raise the running max to the half's true max, rescale O and l (and the
-  // fp16 P of half PENDING, if >= 0, whose P.V is still to come), and recompute P. Wave-uniform.
-  template <int KB, int PENDING>
-  __device__ __forceinline__ float rescale() {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 16; ++t) mx = fmaxf(mx, s[KB][t] * c[KB]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    if (mx > m) {  // false while both are -inf
-      const float alpha = fast_exp2(m - mx);  // m = -inf: alpha = 0 (O and l are still 0)
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i) o[i] *= alpha;
-      if constexpr (PENDING >= 0) {
-        // the pending P is rescaled in fp32 and re-rounded; its share of l is rebuilt from the
-        // re-rounded values, so that O and l keep receiving identical weights
-        const float old_sum = psum<PENDING>();
-#pragma unroll
-        for (int g8 = 0; g8 < 2; ++g8)
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            p[PENDING][g8][e] = static_cast<_Float16>(static_cast<float>(p[PENDING][g8][e]) * alpha);
-        l = (l - old_sum) * alpha + psum<PENDING>();
-      } else {
+        for (int i = 0; i < D / 32; ++i) o[i] *= alpha;
         l *= alpha;
+        m = mx;
+        m_use = mx;
       }
-      m = mx;
-      m_use = mx;
+      rs0 = softmax<0>();
+      rs1 = softmax<1>();
     }
-    return softmax<KB>();
-  }
-
-  // Finish half KB after its softmax: take the slow path if needed, then add the row sum.
-  template <int KB, int PENDING = -1>
-  __device__ __forceinline__ void settle(float rs) {
-    if (__any(row_valid && (!(rs <= P_LIMIT) || m == -INFINITY))) rs = rescale<KB, PENDING>();
-    l += rs;
+    l += rs0 + rs1;
   }
 
   // O^T += V^T P^T for key half KB of the V^T tile in stage vst.
@@ -438,24 +413,6 @@ template <int KB, int D, bool KV8>
 __device__ __forceinline__ void convert_rt(Wave<D, KV8>& wv, bool i8, const float* scl) {
   if (i8) wv.template convert<KB, true>(scl);
   else wv.template convert<KB, false>(scl);
-}
-
-// One main-loop iteration of a run whose tiles n and n+1 share this wave's route I8 and need no
-// mask: the score conversion and softmax of a key half overlap the P.V of the previous half and
-// the score MFMAs of the next one, in straight-line code apart from the rare slow path.
-template <int D, bool KV8, bool I8>
-__device__ __forceinline__ void run_iter(Wave<D, KV8>& wv, const char* vst, const char* kst, const char* q16,
-                                         const float* scl_n, const float* scl_n1) {
-  wv.template convert<1, I8>(scl_n);
-  float rs = wv.template softmax<1>();
-  wv.template pv<0>(vst);
-  wv.template qk<0, I8, false>(kst, q16, nullptr, 0, 0, 1, 0);
-  wv.template settle<1>(rs);
-  wv.template convert<0, I8>(scl_n1);
-  rs = wv.template softmax<0>();
-  wv.template pv<1>(vst);
-  wv.template qk<1, I8, false>(kst, q16, nullptr, 0, 0, 1, 0);
-  wv.template settle<0>(rs);
 }
 
 // Fused Q quantization (the alternative to the quantize-once pass): the two lanes of a query row
@@ -588,7 +545,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) wv.q8f[ks] = *reinterpret_cast<const int4v*>(q8p + 32 * ks + 16 * hl);
     wv.cq = fmaxf(a.q_scale[static_cast<int64_t>(h) * a.total_q + tq] * a.scale_log2, 1e-30f);
-  } else {  // rows past the sequence; with fused quantization the codes are set after the barrier
+  } else {  // rows past the sequence; with fused quantization the codes are set further down
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) wv.q8f[ks] = int4v{};
   }
@@ -612,123 +569,61 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
     dc.act_limit = a.causal ? qlast_w + off : 0x7fffffff;
   }
 
-  // route bits of the workgroup's rows for tiles n, n+1, n+2 (bit r = route row rr0 + r)
-  uint32_t rb0 = 0, rb1 = 0, rb2 = 0, rb3 = 0;
-  if (n_tiles > 0) rb0 = group_bits(wrow, a.wpr, nrr, 0);
-  if (n_tiles > 1) rb1 = (1 % tpg) ? rb0 : group_bits(wrow, a.wpr, nrr, 1 / tpg);
-  if (n_tiles > 2) rb2 = (2 % tpg) ? rb1 : group_bits(wrow, a.wpr, nrr, 2 / tpg);
+  // route bits of the workgroup's rows for tiles n and n+1 (bit r = route row rr0 + r)
+  auto bits_of = [&](int n) { return group_bits(wrow, a.wpr, nrr, n / tpg); };
+  uint32_t rb0 = n_tiles > 0 ? bits_of(0) : 0u;
+  uint32_t rb1 = n_tiles > 1 ? bits_of(1) : 0u;
 
-  // ---- prologue: K tiles 0 and 1, V^T tile 0, factors of tiles 0 and 1
+  // fused Q quantization: each lane quantizes its half of its query row from the fp16 tile in LDS
+  if (a.q8 == nullptr) {
+    __syncthreads();  // publishes the fp16 Q stores
+    if (wv.row_valid)
+      wv.cq = fmaxf(quantize_q_half<D>(q16w, ROWS_W * w + r32, hl, wv.q8f) * a.scale_log2, 1e-30f);
+  }
+
+  // ---- prologue: K, V^T and factors of tile 0
   if (n_tiles > 0) {
     stg.k_next(kbuf, rb0 != full, rb0 != 0u);
     stg.v_next(vbuf);
     stg.s_next(sbuf);
   }
-  if (n_tiles > 1) {
-    stg.k_next(kbuf + L::KSTAGE, rb1 != full, rb1 != 0u);
-    stg.s_next(sbuf + L::SSLOT);
-  }
-  dma_barrier();  // also publishes the fp16 Q stores
-  if (a.q8 == nullptr && wv.row_valid)  // fused: quantize this lane's half of its query row
-    wv.cq = fmaxf(quantize_q_half<D>(q16w, ROWS_W * w + r32, hl, wv.q8f) * a.scale_log2, 1e-30f);
 
-  if (wave_live && n_tiles > 0) {
-    const float* scl0 = reinterpret_cast<const float*>(sbuf);
-    const bool i8 = (rb0 >> my_rl) & 1u;
-    if (i8) {
-      qk_tile<0, true, DUMP>(wv, kbuf, q16w, 0, dc);
-      qk_tile<1, true, DUMP>(wv, kbuf, q16w, 0, dc);
-    } else {
-      qk_tile<0, false, DUMP>(wv, kbuf, q16w, 0, dc);
-      qk_tile<1, false, DUMP>(wv, kbuf, q16w, 0, dc);
+  // ---- main loop: iteration n computes tile n (scores of both halves, their softmax, P.V) while
+  // the direct loads of tile n+1 fly
+  for (int n = 0; n < n_tiles; ++n) {
+    dma_barrier();  // tile n landed; the stages of tile n-1 are free
+    if (n + 1 < n_tiles) {
+      stg.k_next(kbuf + ((n + 1) & 1) * L::KSTAGE, rb1 != full, rb1 != 0u);
+      stg.v_next(vbuf + ((n + 1) & 1) * L::VSTAGE);
+      stg.s_next(sbuf + ((n + 1) & 1) * L::SSLOT);
     }
-    convert_rt<0>(wv, i8, scl0);
-    if (n_full < 1) wv.template mask<0>(0);
-    wv.template settle<0>(wv.template softmax<0>());
-  }
-
-  // ---- main loop: iteration n finishes tile n and starts tile n+1. Runs of iterations whose
-  // two tiles are INT8-routed for this wave and need no mask go through a branch-free specialised
-  // loop; the rest (FP16 tiles, route changes, diagonal and tail tiles, the last tile, the debug
-  // dump) through a generic iteration.
-  int g3 = 2 / tpg, tig3 = 2 % tpg;  // group of tile n+2 and its index within the group
-  int slot_n = 0;                    // factor slot of tile n (tiles rotate through three slots)
-  const bool fast_ok = wave_live && !DUMP;
-
-  // barrier, then the direct loads of K_{n+2}, its factors and V_{n+1}; route bits of tile n+3
-  auto begin_iter = [&](int n) {
-    dma_barrier();  // K_{n+1}, V_n and their factors landed; stages of K_n and V_{n-1} free
-    if (n + 2 < n_tiles) {
-      stg.k_next(kbuf + (n & 1) * L::KSTAGE, rb2 != full, rb2 != 0u);
-      stg.s_next(sbuf + (slot_n == 0 ? 2 : slot_n - 1) * L::SSLOT);
-    }
-    if (n + 1 < n_tiles) stg.v_next(vbuf + ((n + 1) & 1) * L::VSTAGE);
-    rb3 = rb2;
-    if (++tig3 == tpg) {
-      tig3 = 0;
-      ++g3;
-      if (n + 3 < n_tiles) rb3 = group_bits(wrow, a.wpr, nrr, g3);
-    }
-  };
-  auto end_iter = [&]() {
-    rb0 = rb1;
-    rb1 = rb2;
-    rb2 = rb3;
-    slot_n = slot_n == 2 ? 0 : slot_n + 1;
-  };
-  // iteration n can take the specialised loop: tiles n and n+1 exist, are both INT8-routed for
-  // this wave and need no mask (FP16 runs take the generic iteration, which keeps the register
-  // footprint of the kernel within two waves per SIMD)
-  auto fast = [&](int n) {
-    return fast_ok && n + 1 < n_tiles && n + 1 < n_full && (((rb0 & rb1) >> my_rl) & 1u) != 0u;
-  };
-  auto scl_of = [&](int slot) { return reinterpret_cast<const float*>(sbuf + slot * L::SSLOT); };
-  auto slot_next = [&]() { return slot_n == 2 ? 0 : slot_n + 1; };
-
-  for (int n = 0; n < n_tiles;) {
-    if (fast(n)) {
-      do {
-        begin_iter(n);
-        run_iter<D, KV8, true>(wv, vbuf + (n & 1) * L::VSTAGE, kbuf + ((n + 1) & 1) * L::KSTAGE, q16w,
-                               scl_of(slot_n), scl_of(slot_next()));
-        end_iter();
-        ++n;
-      } while (fast(n));
-      continue;
-    }
-    begin_iter(n);
     if (wave_live) {
-      // the two pipeline steps in sequence, with the route and mask chosen at run time (the
-      // compiler may interleave the pieces: fencing them apart measured 5-9 % slower on maps
-      // whose route changes often, and no faster elsewhere)
       const int j0 = n * BN;
-      const bool more = n + 1 < n_tiles;
-      const bool n8 = (rb1 >> my_rl) & 1u;
+      const bool i8 = (rb0 >> my_rl) & 1u;
+      const char* kst = kbuf + (n & 1) * L::KSTAGE;
       const char* vst = vbuf + (n & 1) * L::VSTAGE;
-      const char* kst = kbuf + ((n + 1) & 1) * L::KSTAGE;
-      const float* scl_n1 = scl_of(slot_next());
-      // each half settles before the P.V of the half before it, so its slow path also rescales
-      // that half's pending P
-      const bool c8 = (rb0 >> my_rl) & 1u;
-      convert_rt<1>(wv, c8, scl_of(slot_n));
-      if (n >= n_full) wv.template mask<1>(j0 + 32);
-      wv.template settle<1, 0>(wv.template softmax<1>());
+      const float* scl = reinterpret_cast<const float*>(sbuf + (n & 1) * L::SSLOT);
+      if (i8) {
+        qk_tile<0, true, DUMP>(wv, kst, q16w, j0, dc);
+        qk_tile<1, true, DUMP>(wv, kst, q16w, j0, dc);
+      } else {
+        qk_tile<0, false, DUMP>(wv, kst, q16w, j0, dc);
+        qk_tile<1, false, DUMP>(wv, kst, q16w, j0, dc);
+      }
+      convert_rt<0>(wv, i8, scl);
+      convert_rt<1>(wv, i8, scl);
+      if (n >= n_full) {
+        wv.template mask<0>(j0);
+        wv.template mask<1>(j0 + 32);
+      }
+      const float rs0 = wv.template softmax<0>();
+      const float rs1 = wv.template softmax<1>();
+      wv.settle_tile(rs0, rs1);
       wv.template pv<0>(vst);
-      if (more) {
-        if (n8) qk_tile<0, true, DUMP>(wv, kst, q16w, j0 + BN, dc);
-        else qk_tile<0, false, DUMP>(wv, kst, q16w, j0 + BN, dc);
-        convert_rt<0>(wv, n8, scl_n1);
-        if (n + 1 >= n_full) wv.template mask<0>(j0 + BN);
-        wv.template settle<0, 1>(wv.template softmax<0>());
-      }
       wv.template pv<1>(vst);
-      if (more) {
-        if (n8) qk_tile<1, true, DUMP>(wv, kst, q16w, j0 + BN, dc);
-        else qk_tile<1, false, DUMP>(wv, kst, q16w, j0 + BN, dc);
-      }
     }
-    end_iter();
-    ++n;
+    rb0 = rb1;
+    if (n + 2 < n_tiles) rb1 = ((n + 2) % tpg) ? rb1 : bits_of(n + 2);
   }
 
   // ---- epilogue: O = O^T / l, LSE = (m + log2 l) * ln 2
