@@ -19,14 +19,19 @@
 //     32 rows and 64 keys), so the FP16 / INT8 choice is a wave-uniform branch.
 //
 // Schedule (per wavefront, one 64-key tile per iteration)
-//   After the tile's barrier each wavefront issues the score MFMAs of both 32-key halves, then
-//   converts and exponentiates both (VALU) with one slow-path check for the tile, then issues
-//   both halves' P.V MFMAs; the second half's scores overlap the first half's conversion, and
-//   the other wavefront of the SIMD fills the rest. A deeper software pipeline across tiles
-//   (scores of the next tile during this tile's softmax) measured slower: its extra live
-//   registers pushed the kernel into spills. One barrier per 64-key tile; the next tile's K
-//   (fp16 and/or int8, as the route bits of the workgroup ask), V^T and per-key factors are
-//   fetched with direct global->LDS loads while the current tile is computed.
+//   After the tile's barrier each wavefront reads all K fragments of the tile and issues the
+//   score MFMAs of both 32-key halves (two interleaved accumulator chains), reads the per-key
+//   factors and the first half's V^T fragments, converts and exponentiates both halves (VALU)
+//   with one slow-path check for the tile, then reads the second half's V^T fragments and
+//   issues both halves' P.V MFMAs; the other wavefront of the SIMD fills the gaps. Operand reads
+//   are issued ahead of their MFMAs so that each waits only for its own data: the direct loads
+//   are written as inline assembly, because the compiler counts a pending direct load against
+//   the LDS counter too and would then wait for every LDS read to finish before each MFMA. A
+//   deeper software pipeline across tiles (scores of the next tile during this tile's softmax)
+//   measured slower: its extra live registers pushed the kernel into spills. One barrier per
+//   64-key tile; the next tile's K (fp16 and/or int8, as the route bits of the workgroup ask),
+//   V^T and per-key factors are fetched with direct global->LDS loads while the current tile is
+//   computed.
 //
 // Softmax
 //   Base 2, with the score scale folded into one FMA per element. The running max is only
@@ -39,10 +44,8 @@
 // INT8 scores
 //   The int32 accumulator is converted to fp32 and multiplied by the per-key factor dk' of the
 //   V^T pre-pass, then one FMA with the per-row factor and the running max gives the exponent.
-//   kBiasedI8 selects the alternative in which the accumulator starts at the bit pattern of
-//   1.5 * 2^23 (as |q8 . k8| < 2^22 it then reads as the fp32 number 1.5 * 2^23 + q8 . k8
-//   exactly, and one FMA with (dk', -1.5 * 2^23 * dk') gives dk' * (q8 . k8)); it saves the
-//   conversion but reads twice the factors and measured slower.
+//   (The pre-pass also stores offsets for a form that starts the accumulator at the bit pattern
+//   of 1.5 * 2^23 and rescales with one FMA; it saves the conversion but measured slower.)
 #include "device_types.h"
 #include "launch.h"
 #include "tile_layout.h"
@@ -55,10 +58,6 @@ constexpr int NW = 8;         // wavefronts per workgroup
 constexpr int ROWS_W = 32;    // query rows per wavefront
 constexpr int BM = NW * ROWS_W;
 constexpr float P_LIMIT = 32768.0f;  // fast path: a lane's sum of P over a tile stays below this
-constexpr int I8_BIAS = 0x4B400000;  // fp32 bits of 1.5 * 2^23
-// true: INT8 accumulators start at I8_BIAS and one FMA with (dk', bk) rescales them;
-// false: they start at 0 and are converted, then multiplied by dk'
-constexpr bool kBiasedI8 = false;
 
 // LDS layout. Rows are unpadded; 16-byte chunks are XOR-swizzled per row so that each 1 KiB
 // block stays contiguous (one direct wave load) while the rows one operand read touches fall in
@@ -93,15 +92,17 @@ __device__ __forceinline__ half2v pk(float a, float b) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// One direct global->LDS load per lane: 16 bytes from src to lds_block + 16 * lane.
+// One direct global->LDS load per lane: 16 bytes from src to lds_block + 16 * lane. Written as
+// inline assembly so that the compiler does not track it: every wait for it is explicit
+// (dma_barrier), and the waits for LDS reads can count only the reads.
 __device__ __forceinline__ void dma16(const void* src, char* lds_block) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_block, 16, 0, 0);
+  const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)lds_block));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
 }
 
 // Barrier after direct global->LDS loads. The memory fence of a workgroup barrier does not
-// cover the LDS writes of these loads (the compiler does not count them as LDS stores), so each
-// wave first waits for all of its own outstanding loads (s_waitcnt with every counter at zero);
-// after the barrier every wave's loads have landed.
+// cover the LDS writes of these loads, so each wave first waits for all of its own outstanding
+// loads (s_waitcnt with every counter at zero); after the barrier every wave's loads have landed.
 __device__ __forceinline__ void dma_barrier() {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -248,7 +249,6 @@ struct Wave {
   int kbase8, vbase;      // K8 row (i = ks), V^T row (i = 16-key step)
   int kbase16, qbase16;   // fp16 K and Q rows (i = ks)
   int4v q8f[D / 32];
-  int16v bias;     // starting value of the INT8 accumulators (I8_BIAS or 0)
   float cq;        // q_scale * softmax_scale * log2(e), floored so that 0 * -inf cannot occur
   float cs;        // softmax_scale * log2(e)
   float16v o[D / 32];  // O^T accumulator
@@ -257,71 +257,106 @@ struct Wave {
   half8v p[2][2];      // fp16 P of the two key halves, [half][16-key step]
   float m, m_use, l;   // running max (log2 units), its finite stand-in, this lane's row sum
 
-  // s[KB] = raw scores of key half KB of the K tile in stage kst: int32 accumulators (as bits)
-  // for INT8, fp32 dot products for FP16; convert<KB, I8>() turns them into scores.
-  // With DUMP, the raw int32 accumulators of an INT8 half also go to the debug dump when
-  // dump_row is not NULL: key j of this lane's query row is dump_row[(j / bn_r) * tile_stride +
-  // j % bn_r], for the keys j < Lk; key0 = sequence-local index of the half's first key.
-  // FENCED: the FP16 chain is split by a scheduling fence so that fewer operands are in flight.
-  template <int KB, bool I8, bool DUMP, bool FENCED = false>
-  __device__ __forceinline__ void qk(const char* kst, const char* q16, int32_t* dump_row, int key0, int Lk,
-                                     int bn_r, int tile_stride) {
+  // s[0], s[1] = raw scores of the two key halves of the K tile in stage kst: int32
+  // accumulators (as bits) for INT8, fp32 dot products for FP16; convert_f turns them into
+  // scores. INT8: the eight K fragments are read first, then the two accumulator chains are
+  // interleaved, so each MFMA waits only for its own fragment.
+  __device__ __forceinline__ void qk_i8(const char* kst) {
     using L = Smem<D>;
-    if constexpr (I8) {
-      int16v acc = kBiasedI8 ? bias : int16v{};
+    int4v kf[2][D / 32];
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) {
-        const int4v kf = *reinterpret_cast<const int4v*>(kst + L::K8 + KB * 32 * L::RB8 + (kbase8 ^ (32 * ks)));
-        acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, q8f[ks], acc, 0, 0, 0);
-      }
-      if constexpr (DUMP) {
-        if (dump_row != nullptr) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int t = 0; t < 16; ++t) {
-            const int key = key0 + 16 * (t >> 3) + 8 * hl + (t & 7);
-            if (key < Lk) dump_row[(key / bn_r) * tile_stride + key % bn_r] = acc[t] - (kBiasedI8 ? I8_BIAS : 0);
-          }
-        }
-      }
-      s[KB] = __builtin_bit_cast(float16v, acc);
-    } else {
-      float16v acc = {};
+      for (int ks = 0; ks < D / 32; ++ks)
+        kf[kb][ks] = *reinterpret_cast<const int4v*>(kst + L::K8 + kb * 32 * L::RB8 + (kbase8 ^ (32 * ks)));
+    int16v a0 = {}, a1 = {};
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        // fenced: at most half of the chain's operands in flight
-        if (FENCED && ks == D / 32) __builtin_amdgcn_sched_barrier(0);
-        const half8v qv = *reinterpret_cast<const half8v*>(q16 + (qbase16 ^ (32 * ks)));
-        const half8v kf = *reinterpret_cast<const half8v*>(kst + L::K16 + KB * 32 * L::RB16 + (kbase16 ^ (32 * ks)));
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qv, acc, 0, 0, 0);
+    for (int ks = 0; ks < D / 32; ++ks) {
+      a0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[0][ks], q8f[ks], a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[1][ks], q8f[ks], a1, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 32), 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * (D / 32), 0);
+    s[0] = __builtin_bit_cast(float16v, a0);
+    s[1] = __builtin_bit_cast(float16v, a1);
+  }
+
+  // FP16: the two chains interleaved, one Q fragment feeding both.
+  __device__ __forceinline__ void qk_f16(const char* kst, const char* q16) {
+    using L = Smem<D>;
+    float16v a0 = {}, a1 = {};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const half8v qv = *reinterpret_cast<const half8v*>(q16 + (qbase16 ^ (32 * ks)));
+      const half8v k0 = *reinterpret_cast<const half8v*>(kst + L::K16 + (kbase16 ^ (32 * ks)));
+      const half8v k1 = *reinterpret_cast<const half8v*>(kst + L::K16 + 32 * L::RB16 + (kbase16 ^ (32 * ks)));
+      a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0, qv, a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1, qv, a1, 0, 0, 0);
+    }
+    s[0] = a0;
+    s[1] = a1;
+  }
+
+  // The V^T fragments of key half KB of the tile in stage vst.
+  template <int KB>
+  __device__ __forceinline__ void load_v(const char* vst, half8v (&vf)[2][D / 32]) const {
+#pragma unroll
+    for (int g8 = 0; g8 < 2; ++g8)
+#pragma unroll
+      for (int dblk = 0; dblk < D / 32; ++dblk)
+        vf[g8][dblk] = *reinterpret_cast<const half8v*>(vst + dblk * 32 * (BN * 2) + (vbase ^ (32 * (2 * KB + g8))));
+  }
+
+  // O^T += V^T P^T for key half KB from fragments already in registers.
+  template <int KB>
+  __device__ __forceinline__ void pv_regs(const half8v (&vf)[2][D / 32]) {
+#pragma unroll
+    for (int g8 = 0; g8 < 2; ++g8)
+#pragma unroll
+      for (int dblk = 0; dblk < D / 32; ++dblk)
+        o[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[g8][dblk], p[KB][g8], o[dblk], 0, 0, 0);
+  }
+
+  // Debug dump of the raw INT8 accumulators of both halves (s holds them as bits): key j of
+  // this lane's query row goes to dump_row[(j / bn_r) * tile_stride + j % bn_r], for the keys
+  // j < Lk; key0 = sequence-local index of the tile's first key. Nothing when dump_row is NULL.
+  __device__ __forceinline__ void dump_i8(int32_t* dump_row, int key0, int Lk, int bn_r, int tile_stride) const {
+    if (dump_row == nullptr) return;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int key = key0 + 32 * kb + 16 * (t >> 3) + 8 * hl + (t & 7);
+        const float v = s[kb][t];  // a plain value: bit_cast of a vector element reads element 0
+        if (key < Lk) dump_row[(key / bn_r) * tile_stride + key % bn_r] = __builtin_bit_cast(int, v);
       }
-      s[KB] = acc;
+  }
+
+  // The per-key factors dk' of key half KB, for convert_f.
+  template <int KB>
+  __device__ __forceinline__ void load_f(const float* scl, float4v (&f)[2][2]) const {
+#pragma unroll
+    for (int g8 = 0; g8 < 2; ++g8) {
+      const int kidx = 32 * KB + 16 * g8 + 8 * hl;
+      f[g8][0] = *reinterpret_cast<const float4v*>(scl + kidx);
+      f[g8][1] = *reinterpret_cast<const float4v*>(scl + kidx + 4);
     }
   }
 
-  // Raw scores of half KB -> fp32 scores in units of 1 / c[KB]; scl = the per-key factors of the
-  // half's tile. INT8: dk' * (q8 . k8); FP16: the dot product (times dk' for an INT8 cache).
+  // Raw scores of half KB -> fp32 scores in units of 1 / c[KB], with the half's per-key factors
+  // f in registers. INT8: dk' * (q8 . k8); FP16: the dot product (times dk' for an INT8 cache).
   template <int KB, bool I8>
-  __device__ __forceinline__ void convert(const float* scl) {
+  __device__ __forceinline__ void convert_f(const float4v (&f)[2][2]) {
     if constexpr (I8 || KV8) {
 #pragma unroll
-      for (int g8 = 0; g8 < 2; ++g8) {
-        const int kidx = 32 * KB + 16 * g8 + 8 * hl;
-        const float4v d0 = *reinterpret_cast<const float4v*>(scl + kidx);
-        const float4v d1 = *reinterpret_cast<const float4v*>(scl + kidx + 4);
-        float4v b0 = {}, b1 = {};
-        if constexpr (I8 && kBiasedI8) {
-          b0 = *reinterpret_cast<const float4v*>(scl + BN + kidx);
-          b1 = *reinterpret_cast<const float4v*>(scl + BN + kidx + 4);
-        }
+      for (int g8 = 0; g8 < 2; ++g8)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float dk = e < 4 ? d0[e] : d1[e - 4];
+          const float dk = f[g8][e >> 2][e & 3];
           const float v = s[KB][8 * g8 + e];
           if constexpr (!I8) s[KB][8 * g8 + e] = v * dk;
-          else if constexpr (kBiasedI8) s[KB][8 * g8 + e] = __builtin_fmaf(v, dk, e < 4 ? b0[e] : b1[e - 4]);
           else s[KB][8 * g8 + e] = static_cast<float>(__builtin_bit_cast(int, v)) * dk;
         }
-      }
     }
     c[KB] = I8 ? cq : cs;
   }
@@ -378,42 +413,14 @@ struct Wave {
     l += rs0 + rs1;
   }
 
-  // O^T += V^T P^T for key half KB of the V^T tile in stage vst.
-  template <int KB>
-  __device__ __forceinline__ void pv(const char* vst) {
-#pragma unroll
-    for (int g8 = 0; g8 < 2; ++g8) {
-      const int kk = 2 * KB + g8;
-#pragma unroll
-      for (int dblk = 0; dblk < D / 32; ++dblk) {
-        const half8v vf = *reinterpret_cast<const half8v*>(vst + dblk * 32 * (BN * 2) + (vbase ^ (32 * kk)));
-        o[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, p[KB][g8], o[dblk], 0, 0, 0);
-      }
-    }
-  }
 };
 
 // Where the debug dump of the current tiles goes (DUMP instances only).
 struct DumpCtx {
-  int32_t* row;  // this lane's query row in the dump (NULL: not dumped); see Wave::qk
+  int32_t* row;  // this lane's query row in the dump (NULL: not dumped); see Wave::dump_i8
   int bn_r, tile_stride, Lk;
   int act_limit;  // a key tile starting at j0 is dumped iff j0 <= act_limit
 };
-
-// Scores of half KB of the tile at key j0 with the route chosen by I8 (and the dump, if any).
-template <int KB, bool I8, bool DUMP, int D, bool KV8>
-__device__ __forceinline__ void qk_tile(Wave<D, KV8>& wv, const char* kst, const char* q16, int j0,
-                                        const DumpCtx& dc) {
-  int32_t* row = (DUMP && I8 && j0 <= dc.act_limit) ? dc.row : nullptr;
-  wv.template qk<KB, I8, DUMP, true>(kst, q16, row, j0 + 32 * KB, dc.Lk, dc.bn_r, dc.tile_stride);
-}
-
-// convert<KB, I8>() with the route chosen at run time.
-template <int KB, int D, bool KV8>
-__device__ __forceinline__ void convert_rt(Wave<D, KV8>& wv, bool i8, const float* scl) {
-  if (i8) wv.template convert<KB, true>(scl);
-  else wv.template convert<KB, false>(scl);
-}
 
 // Fused Q quantization (the alternative to the quantize-once pass): the two lanes of a query row
 // (hl = 0, 1) each read, from the workgroup's fp16 Q in LDS, the channels [32 ks + 16 hl, +16)
@@ -525,8 +532,6 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
     wv.kbase8 = kr * L::RB8 + 16 * (hl ^ L::f8(kr));
     wv.vbase = r32 * (BN * 2) + 16 * (hl ^ vt_swizzle(r32));
   }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) wv.bias[i] = kBiasedI8 ? I8_BIAS : 0;
 
   // ---- resident queries: fp16 Q of the workgroup in LDS, this wave's int8 Q in registers
   for (int ch = tid; ch < BM * L::C16; ch += NW * 64) {
@@ -604,14 +609,23 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
       const char* vst = vbuf + (n & 1) * L::VSTAGE;
       const float* scl = reinterpret_cast<const float*>(sbuf + (n & 1) * L::SSLOT);
       if (i8) {
-        qk_tile<0, true, DUMP>(wv, kst, q16w, j0, dc);
-        qk_tile<1, true, DUMP>(wv, kst, q16w, j0, dc);
+        wv.qk_i8(kst);
+        if constexpr (DUMP) wv.dump_i8(j0 <= dc.act_limit ? dc.row : nullptr, j0, dc.Lk, dc.bn_r, dc.tile_stride);
       } else {
-        qk_tile<0, false, DUMP>(wv, kst, q16w, j0, dc);
-        qk_tile<1, false, DUMP>(wv, kst, q16w, j0, dc);
+        wv.qk_f16(kst, q16w);
       }
-      convert_rt<0>(wv, i8, scl);
-      convert_rt<1>(wv, i8, scl);
+      float4v f0[2][2], f1[2][2];
+      half8v vf0[2][D / 32];
+      wv.template load_f<0>(scl, f0);
+      wv.template load_f<1>(scl, f1);
+      wv.template load_v<0>(vst, vf0);
+      if (i8) {
+        wv.template convert_f<0, true>(f0);
+        wv.template convert_f<1, true>(f1);
+      } else {
+        wv.template convert_f<0, false>(f0);
+        wv.template convert_f<1, false>(f1);
+      }
       if (n >= n_full) {
         wv.template mask<0>(j0);
         wv.template mask<1>(j0 + 32);
@@ -619,8 +633,13 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
       const float rs0 = wv.template softmax<0>();
       const float rs1 = wv.template softmax<1>();
       wv.settle_tile(rs0, rs1);
-      wv.template pv<0>(vst);
-      wv.template pv<1>(vst);
+      half8v vf1[2][D / 32];
+      wv.template load_v<1>(vst, vf1);
+      wv.template pv_regs<0>(vf0);
+      wv.template pv_regs<1>(vf1);
+      // the second half's V^T reads first, then all P.V MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 32), 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * (D / 32), 0);
     }
     rb0 = rb1;
     if (n + 2 < n_tiles) rb1 = ((n + 2) % tpg) ? rb1 : bits_of(n + 2);
