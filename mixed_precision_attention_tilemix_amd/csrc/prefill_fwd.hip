@@ -578,6 +578,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
   auto bits_of = [&](int n) { return group_bits(wrow, a.wpr, nrr, n / tpg); };
   uint32_t rb0 = n_tiles > 0 ? bits_of(0) : 0u;
   uint32_t rb1 = n_tiles > 1 ? bits_of(1) : 0u;
+  int pos2 = 2 % tpg, grp2 = 2 / tpg;  // routing group of tile 2 and the tile's place in it
 
   // fused Q quantization: each lane quantizes its half of its query row from the fp16 tile in LDS
   if (a.q8 == nullptr) {
@@ -642,7 +643,12 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
       __builtin_amdgcn_sched_group_barrier(0x008, 4 * (D / 32), 0);
     }
     rb0 = rb1;
-    if (n + 2 < n_tiles) rb1 = ((n + 2) % tpg) ? rb1 : bits_of(n + 2);
+    // tile n+2's position in its routing group, kept as a counter (no division per tile)
+    if (pos2 == 0 && n + 2 < n_tiles) rb1 = group_bits(wrow, a.wpr, nrr, grp2);
+    if (++pos2 == tpg) {
+      pos2 = 0;
+      ++grp2;
+    }
   }
 
   // ---- epilogue: O = O^T / l, LSE = (m + log2 l) * ln 2
