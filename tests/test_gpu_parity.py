@@ -338,20 +338,36 @@ def test_int32_dump_bit_exact(shape):
 
 @pytest.mark.parametrize("name", ["mha8k", "gqa32k", "varlen64k", "kvint8_128k"])
 def test_full_size_sampled_parity(name):
+    """Sampled rows of the full-size workloads against the oracle, in two launch configurations:
+    quantize-once with fp32 output, and the configuration bench.py times (Q quantized inside the
+    fused kernel, fp16 output)."""
     w = named(name)
-    prob = run(w)
     rows = sample_rows(w)
     ref, ref_lse, n8, nall = oracle.prepare(w).prefill(rows)
-    out = prob.out[torch.from_numpy(rows).cuda()].cpu().numpy()
-    err = check_out(out, ref, name)
-    check_lse(prob.lse[:, torch.from_numpy(rows).cuda()].cpu().numpy(), ref_lse, name)
-    print(f"{name}: {len(rows)} rows x {w.hq} heads, max err {err:.2e}, INT8 pairs {n8 / nall:.3f}")
+    idx = torch.from_numpy(rows).cuda()
+    prob = run(w)
+    err = check_out(prob.out[idx].cpu().numpy(), ref, name)
+    check_lse(prob.lse[:, idx].cpu().numpy(), ref_lse, name)
+    del prob
+    bench_cfg = DeviceProblem(w, out_dtype=torch.float16, fused_q=True)
+    bench_cfg.step()
+    torch.cuda.synchronize()
+    err16 = check_out(bench_cfg.out[idx].float().cpu().numpy(), ref, name + " (fused Q, fp16 out)", fp16_out=True)
+    check_lse(bench_cfg.lse[:, idx].cpu().numpy(), ref_lse, name + " (fused Q, fp16 out)")
+    print(f"{name}: {len(rows)} rows x {w.hq} heads, max err {err:.2e} (fp32 out), {err16:.2e} "
+          f"(fused Q, fp16 out), INT8 pairs {n8 / nall:.3f}")
 
 
 @pytest.mark.parametrize("name", ["gqa32k", "kvint8_128k"])
 def test_full_size_int32_dump(name):
+    """Dumped int32 accumulators of the first, middle and last query tiles, with Q quantized by the
+    quantize-once pass and inside the fused kernel (the configuration bench.py times)."""
     w = named(name)
-    prob = run(w)
     last = w.total_mtiles - 1
-    for m0 in (0, last // 2, last):
-        compare_dump(w, prob, w.hq - 1, m0, 1)
+    for fused in (False, True):
+        prob = DeviceProblem(w, out_dtype=torch.float16 if fused else torch.float32, fused_q=fused)
+        prob.step()
+        torch.cuda.synchronize()
+        for m0 in (0, last // 2, last):
+            compare_dump(w, prob, w.hq - 1, m0, 1)
+        del prob
