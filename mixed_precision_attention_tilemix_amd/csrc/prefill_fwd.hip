@@ -44,8 +44,12 @@
 // INT8 scores
 //   The int32 accumulator is converted to fp32 and multiplied by the per-key factor dk' of the
 //   V^T pre-pass, then one FMA with the per-row factor and the running max gives the exponent.
+//   The factors reach the multiply through a DPP row broadcast: each lane loads one factor per
+//   32-key half and accumulator slot t takes it from lane t of its 16-lane row.
 //   (The pre-pass also stores offsets for a form that starts the accumulator at the bit pattern
 //   of 1.5 * 2^23 and rescales with one FMA; it saves the conversion but measured slower.)
+#include <utility>
+
 #include "device_types.h"
 #include "launch.h"
 #include "tile_layout.h"
@@ -85,6 +89,12 @@ struct Smem {
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Lane T of the calling lane's 16-lane row (DPP row_newbcast; folds into the consuming VALU op).
+template <int T>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + T, 0xF, 0xF, false));
+}
 
 __device__ __forceinline__ half2v pk(float a, float b) {
   return half2v{static_cast<_Float16>(a), static_cast<_Float16>(b)};  // v_cvt_pk_f16_f32 (RNE)
@@ -248,6 +258,7 @@ struct Wave {
   // multiple of 128 bytes sits at row_start + 16*(hl ^ f) XOR 32*i, since 2*i + hl = 2*i ^ hl
   int kbase8, vbase;      // K8 row (i = ks), V^T row (i = 16-key step)
   int kbase16, qbase16;   // fp16 K and Q rows (i = ks)
+  int fkey;               // key (within a 32-key half) whose factor this lane loads for its row
   int4v q8f[D / 32];
   float cq;        // q_scale * softmax_scale * log2(e), floored so that 0 * -inf cannot occur
   float cs;        // softmax_scale * log2(e)
@@ -332,33 +343,26 @@ struct Wave {
       }
   }
 
-  // The per-key factors dk' of key half KB, for convert_f.
+  // The per-key factor dk' of key half KB that this lane's 16-lane row broadcasts: lane i of a
+  // row holds the factor of accumulator slot i of the row's lanes (key 16 (i / 8) + 8 hl + i % 8
+  // of the half), so slot t reads it from lane t of its own row (DPP row_newbcast), and one
+  // 4-byte LDS read per lane replaces the sixteen factors each lane would otherwise load.
   template <int KB>
-  __device__ __forceinline__ void load_f(const float* scl, float4v (&f)[2][2]) const {
-#pragma unroll
-    for (int g8 = 0; g8 < 2; ++g8) {
-      const int kidx = 32 * KB + 16 * g8 + 8 * hl;
-      f[g8][0] = *reinterpret_cast<const float4v*>(scl + kidx);
-      f[g8][1] = *reinterpret_cast<const float4v*>(scl + kidx + 4);
-    }
+  __device__ __forceinline__ float load_f(const float* scl) const {
+    return scl[32 * KB + fkey];
   }
 
   // Raw scores of half KB -> fp32 scores in units of 1 / c[KB], with the half's per-key factors
-  // f in registers. INT8: dk' * (q8 . k8); FP16: the dot product (times dk' for an INT8 cache).
+  // broadcast from fr. INT8: dk' * (q8 . k8); FP16: the dot product (times dk' for an INT8 cache).
   template <int KB, bool I8>
-  __device__ __forceinline__ void convert_f(const float4v (&f)[2][2]) {
-    if constexpr (I8 || KV8) {
-#pragma unroll
-      for (int g8 = 0; g8 < 2; ++g8)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float dk = f[g8][e >> 2][e & 3];
-          const float v = s[KB][8 * g8 + e];
-          if constexpr (!I8) s[KB][8 * g8 + e] = v * dk;
-          else s[KB][8 * g8 + e] = static_cast<float>(__builtin_bit_cast(int, v)) * dk;
-        }
-    }
+  __device__ __forceinline__ void convert_f(float fr) {
+    if constexpr (I8 || KV8) convert_slots<KB, I8>(fr, std::make_integer_sequence<int, 16>{});
     c[KB] = I8 ? cq : cs;
+  }
+  template <int KB, bool I8, int... T>
+  __device__ __forceinline__ void convert_slots(float fr, std::integer_sequence<int, T...>) {
+    ((s[KB][T] = (I8 ? static_cast<float>(__builtin_bit_cast(int, static_cast<float>(s[KB][T])))
+                     : static_cast<float>(s[KB][T])) * row_bcast<T>(fr)), ...);
   }
 
   // Legality mask of half KB (causal diagonal, sequence tail): illegal scores become -inf.
@@ -531,6 +535,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
     wv.qbase16 = (ROWS_W * w + r32) * L::RB16 + 16 * (hl ^ L::f16(ROWS_W * w + r32));
     wv.kbase8 = kr * L::RB8 + 16 * (hl ^ L::f8(kr));
     wv.vbase = r32 * (BN * 2) + 16 * (hl ^ vt_swizzle(r32));
+    wv.fkey = 16 * ((lane & 15) >> 3) + 8 * hl + (lane & 7);
   }
 
   // ---- resident queries: fp16 Q of the workgroup in LDS, this wave's int8 Q in registers
@@ -615,10 +620,9 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
       } else {
         wv.qk_f16(kst, q16w);
       }
-      float4v f0[2][2], f1[2][2];
+      const float f0 = wv.template load_f<0>(scl);
+      const float f1 = wv.template load_f<1>(scl);
       half8v vf0[2][D / 32];
-      wv.template load_f<0>(scl, f0);
-      wv.template load_f<1>(scl, f1);
       wv.template load_v<0>(vst, vf0);
       if (i8) {
         wv.template convert_f<0, true>(f0);
