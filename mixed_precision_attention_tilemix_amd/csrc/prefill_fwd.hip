@@ -102,12 +102,14 @@ __device__ __forceinline__ half2v pk(float a, float b) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// One direct global->LDS load per lane: 16 bytes from src to lds_block + 16 * lane. Written as
-// inline assembly so that the compiler does not track it: every wait for it is explicit
-// (dma_barrier), and the waits for LDS reads can count only the reads.
-__device__ __forceinline__ void dma16(const void* src, char* lds_block) {
+// One direct global->LDS load per lane: 16 bytes from base + voff (base wave-uniform, in scalar
+// registers; voff this lane's 32-bit byte offset) to lds_block + 16 * lane. The scalar-base form
+// needs no per-load address arithmetic on the VALU. Written as inline assembly so that the
+// compiler does not track it: every wait for it is explicit (dma_barrier), and the waits for LDS
+// reads can count only the reads.
+__device__ __forceinline__ void dma16(const char* base, uint32_t voff, char* lds_block) {
   const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)lds_block));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
 }
 
 // Barrier after direct global->LDS loads. The memory fence of a workgroup barrier does not
@@ -190,24 +192,24 @@ struct Stager {
       if (need16) {
 #pragma unroll
         for (int i = 0; i < I16; ++i)
-          if (w + NW * i < NB16) dma16(k16 + o16[i], buf + L::K16 + (w + NW * i) * 1024);
+          if (w + NW * i < NB16) dma16(k16, o16[i], buf + L::K16 + (w + NW * i) * 1024);
       }
       if (need8) {
 #pragma unroll
         for (int i = 0; i < I8; ++i)
-          if (w + NW * i < NB8) dma16(k8 + o8[i], buf + L::K8 + (w + NW * i) * 1024);
+          if (w + NW * i < NB8) dma16(k8, o8[i], buf + L::K8 + (w + NW * i) * 1024);
       }
     } else {
       const int last = Lk - 1 - kn * BN;
       if (need16) {
 #pragma unroll
         for (int i = 0; i < I16; ++i)
-          if (w + NW * i < NB16) dma16(k16 + off16(lane, i, last), buf + L::K16 + (w + NW * i) * 1024);
+          if (w + NW * i < NB16) dma16(k16, off16(lane, i, last), buf + L::K16 + (w + NW * i) * 1024);
       }
       if (need8) {
 #pragma unroll
         for (int i = 0; i < I8; ++i)
-          if (w + NW * i < NB8) dma16(k8 + off8(lane, i, last), buf + L::K8 + (w + NW * i) * 1024);
+          if (w + NW * i < NB8) dma16(k8, off8(lane, i, last), buf + L::K8 + (w + NW * i) * 1024);
       }
     }
     k16 += BN * st16;
@@ -220,13 +222,13 @@ struct Stager {
     __builtin_assume(w >= 0 && w < NW);
 #pragma unroll
     for (int i = 0; i < IV; ++i)
-      if (w + NW * i < NBV) dma16(vt + (w + NW * i) * 1024 + ov, buf + (w + NW * i) * 1024);
+      if (w + NW * i < NBV) dma16(vt + (w + NW * i) * 1024, ov, buf + (w + NW * i) * 1024);
     vt += D * BN * 2;
   }
 
   // The 512 bytes of per-key factors of the next factor tile into a factor slot.
   __device__ __forceinline__ void s_next(char* buf) {
-    if (w == NW - 1 && (threadIdx.x & 63) < 32) dma16(ks + ov, buf);
+    if (w == NW - 1 && (threadIdx.x & 63) < 32) dma16(ks, ov, buf);
     ks += 2 * BN * 4;
   }
 };
