@@ -1,0 +1,62 @@
+"""Host-side logic of bench.py that runs without a GPU: the oracle's row sample, the legal-pair
+counts behind the roofline, and the quoted context figures."""
+
+from types import SimpleNamespace
+
+import numpy as np
+import pytest
+
+import bench
+from mixed_precision_attention_tilemix_amd import workloads as wl
+
+
+def legal_keys(w, rows):
+    """Legal keys of each sampled query row (sequence-local causal prefix, or the whole sequence)."""
+    cu = np.asarray(w.cu_seqlens, dtype=np.int64)
+    b = np.searchsorted(cu, rows, side="right") - 1
+    local = rows - cu[b]
+    return local + 1 if w.causal else (cu[b + 1] - cu[b])
+
+
+@pytest.mark.parametrize("name", ["tiny", "mha8k", "gqa32k", "varlen64k"])
+def test_baseline_rows_sample(name):
+    w = wl.make(name)
+    rows, stride = bench.baseline_rows(w)
+    assert rows.dtype == np.int64 and rows.ndim == 1 and len(rows) > 0
+    assert np.all(np.diff(rows) > 0), "rows sorted and unique"
+    assert rows[0] == 0 and rows[-1] < w.total
+    assert rows[-1] >= w.total - 2 * w.bm_r, "the sample reaches the end of the token range"
+    pairs = int(legal_keys(w, rows).sum()) * w.hq
+    assert pairs <= bench.SAMPLE_PAIRS
+    assert stride >= 1 and stride & (stride - 1) == 0
+
+
+def shape_only(seqlens, hq, bm_r=128, causal=True):
+    """The fields baseline_rows reads, without generating tensors."""
+    cu = np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int64)
+    mt = sum(-(-L // bm_r) for L in seqlens)
+    return SimpleNamespace(cu_seqlens=cu, total=int(cu[-1]), total_mtiles=mt, bm_r=bm_r,
+                           causal=causal, hq=hq)
+
+
+def test_baseline_rows_stride_grows_with_size():
+    _, s_small = bench.baseline_rows(shape_only([8192], 32))
+    rows, s_big = bench.baseline_rows(shape_only([131072], 32))
+    assert s_small == 1 and s_big > 1
+    assert int(legal_keys(shape_only([131072], 32), rows).sum()) * 32 <= bench.SAMPLE_PAIRS
+
+
+def test_int8_pair_counts_closed_forms():
+    # all-INT8 and all-FP16 routing: the INT8 count is every legal pair or none
+    for route, frac in (("int8", 1.0), ("fp16", 0.0)):
+        w = wl.custom([300, 77, 513], 4, 2, 64, bm_r=64, bn_r=64, route=route, seed=1)
+        n8 = bench.int8_pair_counts(w)
+        total = sum(L * (L + 1) // 2 for L in w.seqlens) * w.hq
+        assert n8 == int(frac * total)
+
+
+def test_pages_context_is_marked_as_context():
+    c = bench.PAGES_CONTEXT
+    assert c["hardware"].startswith("NVIDIA A100")
+    assert c["flashattention_fp16"] == 14.33 and c["tilemix_75pct_groups_int8"] == 31.80
+    assert "not comparable" in c["note"]
