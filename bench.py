@@ -136,9 +136,29 @@ def baseline_rows(w):
         stride *= 2
 
 
-def cpu_baseline(w, prob, rows, stride):
+def oracle_problem(w, scale_blocks=None):
+    """The oracle's problem for workload w: per-token codes, or with scale_blocks = (bq, bk) the
+    oracle's block-wise codes of Q and K (K of the INT8 cache included)."""
     import oracle
-    prep = oracle.prepare(w)
+    if scale_blocks is None:
+        return oracle.prepare(w)
+    bq, bk = scale_blocks
+    q8, qs = oracle.quantize_blocks(w.q, w.cu_seqlens, bq)
+    k8, ks = oracle.quantize_blocks(w.k, w.cu_seqlens, bk)
+    extra = {}
+    if w.kv_int8:
+        v8, vs = oracle.quantize_rows(w.v)
+        extra = dict(v8=v8, v_scale=vs)
+    return oracle.Prepared(q=w.q, k=None if w.kv_int8 else w.k, v=None if w.kv_int8 else w.v,
+                           cu_q=w.cu_seqlens, cu_k=w.cu_seqlens, cu_mtiles=w.cu_mtiles, hq=w.hq,
+                           hk=w.hk, d=w.d, words=oracle.pack_route(w.route, w.words_per_row),
+                           bm_r=w.bm_r, bn_r=w.bn_r, group=w.group, causal=w.causal, q8=q8,
+                           q_scale=qs, k8=k8, k_scale=ks, kv_int8=w.kv_int8, **extra)
+
+
+def cpu_baseline(w, prob, rows, stride, scale_blocks=None):
+    import oracle
+    prep = oracle_problem(w, scale_blocks)
     t0 = time.perf_counter()
     out, _, n8, nall = prep.prefill(rows)
     dt = time.perf_counter() - t0
@@ -548,8 +568,14 @@ def main():
     ap.add_argument("--quantize-once", action="store_true",
                     help="quantize Q in a separate pass before the attention call (default: the "
                          "attention kernel quantizes Q itself, with bit-identical codes)")
+    ap.add_argument("--scale-blocks", default=None, metavar="BQ,BK",
+                    help="prefill on block-wise scales: Q and K quantized with one scale per BQ query / "
+                         "BK key tokens of a sequence (tilemix_quantize_blocks); a BK multiple of 64 "
+                         "lets the attention kernel take one K scale per key tile")
     args = ap.parse_args()
-    args.fused_q = not args.quantize_once
+    args.scale_blocks = tuple(int(x) for x in args.scale_blocks.split(",")) if args.scale_blocks else None
+    # Q stays fused (per token) when its blocks are single tokens
+    args.fused_q = not args.quantize_once and (args.scale_blocks is None or args.scale_blocks[0] == 1)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards by KV head with no exchange; see the design notes)", file=sys.stderr)
@@ -576,7 +602,7 @@ def main():
     binding.load()
     calibration_copy()
     w = workloads.make(args.workload)
-    prob = DeviceProblem(w, out_dtype=torch.float16, fused_q=args.fused_q)
+    prob = DeviceProblem(w, out_dtype=torch.float16, fused_q=args.fused_q, scale_blocks=args.scale_blocks)
     stream = torch.cuda.current_stream()
 
     pairs_per_head = w.legal_pairs()
@@ -632,7 +658,9 @@ def main():
             "hq": w.hq, "hkv": w.hk, "head_dim": w.d, "causal": w.causal,
             "route_tile": [w.bm_r, w.bn_r], "group": w.group, "policy": w.policy,
             "int8_pair_fraction": round(r, 4), "out_dtype": "fp16",
-            "q_quantization": "fused" if args.fused_q else "once",
+            "q_quantization": ("fused" if args.fused_q else "once") if args.scale_blocks is None
+                              else f"blocks of {args.scale_blocks[0]} (Q) / {args.scale_blocks[1]} (K) tokens",
+            "k_scale_block": prob.k_scale_block,
         },
         "pct_mixed_roofline": round(100 * tflops / peak_mixed, 2),
         "pct_fp16_roofline": round(100 * tflops / PEAK_FP16, 2),
@@ -646,7 +674,8 @@ def main():
             "peak": round(peak_mixed, 1),
             "unit": "TFLOP/s",
             "frac": round(fwd_tflops / peak_mixed, 4),
-            "traffic": measured_traffic() if args.workload == WORKLOAD else None,
+            # the committed counters were taken on this workload's default configuration only
+            "traffic": measured_traffic() if (args.workload == WORKLOAD and args.fused_q) else None,
             "flops_per_launch": flops,
             "peak_note": f"mixed MFMA peak for INT8 fraction {r:.4f}: INT8 QK^T at {PEAK_INT8}, "
                          f"FP16 QK^T and P.V at {PEAK_FP16} TFLOP/s",
@@ -655,7 +684,7 @@ def main():
     result["context"] = PAGES_CONTEXT
     if not args.no_cpu_baseline:
         rows, stride = baseline_rows(w)
-        result["cpu_baseline"] = cpu_baseline(w, prob, rows, stride)
+        result["cpu_baseline"] = cpu_baseline(w, prob, rows, stride, args.scale_blocks)
     print(json.dumps(result), flush=True)
 
 

@@ -156,6 +156,14 @@ typedef struct tilemix_fwd_params {
    * share one workspace must not overlap in time. */
   void* workspace;
   int64_t workspace_bytes;
+
+  /* 0, or a multiple of 64: the caller guarantees that k_scale is constant over blocks of
+   * k_scale_block keys counted from the first key of each sequence (as tilemix_quantize_blocks
+   * writes them with block_rows = k_scale_block; the blockwise quantization with per-block
+   * scales of Section 4.3). tilemix_prefill_fwd then takes one K scale per 64-key tile (that of
+   * its first key) instead of one per key. Any other k_scale content with a nonzero value is
+   * undefined. tilemix_decode_fwd ignores it. */
+  int32_t k_scale_block;
 } tilemix_fwd_params;
 
 /*
@@ -189,8 +197,8 @@ tilemix_status tilemix_prefill_workspace_size(const tilemix_fwd_params* params, 
  *
  * Errors: EINVAL for a NULL required pointer, struct_size mismatch, hq % hkv != 0,
  * route_block_m not a multiple of 32, route_block_n not a multiple of 64, route_group < 1,
- * words_per_row < 1, kv_int8 with non-NULL k/v (or without v8/v_scale), a bad debug range,
- * a NULL, misaligned or too small workspace; EUNSUPPORTED for head_dim other than 64/128.
+ * k_scale_block negative or not a multiple of 64, words_per_row < 1, kv_int8 with non-NULL
+ * k/v (or without v8/v_scale), a bad debug range, a NULL, misaligned or too small workspace; EUNSUPPORTED for head_dim other than 64/128.
  */
 tilemix_status tilemix_prefill_fwd(const tilemix_fwd_params* params, void* stream);
 

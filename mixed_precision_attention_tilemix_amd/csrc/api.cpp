@@ -127,6 +127,7 @@ tilemix::FwdArgs fwd_args(const tilemix_fwd_params* p) {
   a.dump_m0 = p->debug_mtile_begin;
   a.dump_mcount = p->debug_mtile_count;
   a.dump_ntiles = p->debug_ntiles_max;
+  a.k_block = p->k_scale_block;
   return a;
 }
 
@@ -331,6 +332,9 @@ tilemix_status tilemix_prefill_fwd(const tilemix_fwd_params* p, void* stream) {
       return fail(TILEMIX_EINVAL, "prefill_fwd: debug_ntiles_max %d < ceil(max_seqlen_k / route_block_n)",
                   p->debug_ntiles_max);
   }
+  if (p->k_scale_block < 0 || p->k_scale_block % tilemix::kKeyTile)
+    return fail(TILEMIX_EINVAL, "prefill_fwd: k_scale_block %d is not 0 or a multiple of %d", p->k_scale_block,
+                tilemix::kKeyTile);
   const WorkspaceLayout ws = workspace_layout(p);
   if (p->workspace == nullptr || !aligned(p->workspace, 256) || p->workspace_bytes < ws.total)
     return fail(TILEMIX_EINVAL, "prefill_fwd: workspace must be 256-byte aligned and hold %lld bytes (got %lld)",

@@ -58,6 +58,7 @@ struct FwdArgs {
   float* ks_ws;           // [hkv][vt_tiles][2][64] per-key score factors dk' and -1.5*2^23*dk'
   const float* ks;        // the same, read-only view
   _Float16* k16_ws;       // INT8 cache only: exact fp16(k8) [total_k, hkv, D]
+  int32_t k_block;        // > 0: K scales constant over 64-key tiles (one factor per tile)
 };
 
 // V^T tiles (and, with an INT8 cache, fp16 K) into the workspace; must precede launch_prefill.

@@ -250,8 +250,10 @@ __device__ __forceinline__ uint32_t group_bits(const const_u64* wrow, int wpr, i
   return bits;
 }
 
-// Per-wavefront registers: constants of the wave's rows and the online-softmax state.
-template <int D, bool KV8>
+// Per-wavefront registers: constants of the wave's rows and the online-softmax state. KBLK: the K
+// scales are constant over each 64-key tile (block-wise K quantization), so one factor per tile
+// is folded into the per-row factor instead of multiplying every score.
+template <int D, bool KV8, bool KBLK>
 struct Wave {
   int hl, my_q;
   int lim;         // last legal key (sequence-local) of this lane's query
@@ -351,6 +353,7 @@ struct Wave {
   // 4-byte LDS read per lane replaces the sixteen factors each lane would otherwise load.
   template <int KB>
   __device__ __forceinline__ float load_f(const float* scl) const {
+    if constexpr (KBLK) return scl[0];  // the tile's one factor (that of its first key)
     return scl[32 * KB + fkey];
   }
 
@@ -358,8 +361,21 @@ struct Wave {
   // broadcast from fr. INT8: dk' * (q8 . k8); FP16: the dot product (times dk' for an INT8 cache).
   template <int KB, bool I8>
   __device__ __forceinline__ void convert_f(float fr) {
-    if constexpr (I8 || KV8) convert_slots<KB, I8>(fr, std::make_integer_sequence<int, 16>{});
-    c[KB] = I8 ? cq : cs;
+    if constexpr (KBLK) {
+      // one factor for the whole tile: into the per-row factor (floored, as cq, so that a masked
+      // -inf score never meets a zero factor)
+      if constexpr (I8) {
+#pragma unroll
+        for (int t = 0; t < 16; ++t)
+          s[KB][t] = static_cast<float>(__builtin_bit_cast(int, static_cast<float>(s[KB][t])));
+        c[KB] = fmaxf(cq * fr, 1e-30f);
+      } else {
+        c[KB] = KV8 ? fmaxf(cs * fr, 1e-30f) : cs;
+      }
+    } else {
+      if constexpr (I8 || KV8) convert_slots<KB, I8>(fr, std::make_integer_sequence<int, 16>{});
+      c[KB] = I8 ? cq : cs;
+    }
   }
   template <int KB, bool I8, int... T>
   __device__ __forceinline__ void convert_slots(float fr, std::integer_sequence<int, T...>) {
@@ -470,7 +486,7 @@ __device__ __forceinline__ float quantize_q_half(const char* q16, int row, int h
   return s;
 }
 
-template <int D, bool KV8, bool DUMP>
+template <int D, bool KV8, bool DUMP, bool KBLK>
 __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a) {
   using L = Smem<D>;
   __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
@@ -526,7 +542,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
   char* const sbuf = smem + L::SBUF;
   const char* const q16w = smem + L::Q16;
 
-  Wave<D, KV8> wv;
+  Wave<D, KV8, KBLK> wv;
   wv.hl = hl;
   wv.my_q = qa + r32;
   wv.lim = a.causal ? min(Lk - 1, wv.my_q + off) : Lk - 1;
@@ -696,10 +712,13 @@ hipError_t launch_t(const FwdArgs& a, int32_t batch, hipStream_t stream) {
   if (n_ct == 0 || batch == 0) return hipSuccess;
   dim3 grid(static_cast<unsigned>(a.hq), static_cast<unsigned>(n_ct), static_cast<unsigned>(batch));
   // the debug dump of the INT8 accumulators is compiled into a separate instance of the kernel
+  // (with the dump the per-key instance runs: block-wise scales are per-key scales too)
   if (a.dump != nullptr)
-    prefill_fwd_kernel<D, KV8, true><<<grid, dim3(NW * 64), 0, stream>>>(a);
+    prefill_fwd_kernel<D, KV8, true, false><<<grid, dim3(NW * 64), 0, stream>>>(a);
+  else if (a.k_block > 0)
+    prefill_fwd_kernel<D, KV8, false, true><<<grid, dim3(NW * 64), 0, stream>>>(a);
   else
-    prefill_fwd_kernel<D, KV8, false><<<grid, dim3(NW * 64), 0, stream>>>(a);
+    prefill_fwd_kernel<D, KV8, false, false><<<grid, dim3(NW * 64), 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -22,18 +22,25 @@ class DeviceProblem:
     With ``fused_q`` the fused kernel quantizes Q itself (q8 / q_scale passed as NULL) and the
     quantize step covers K only. With ``scale_blocks=(bq, bk)`` Q and K are quantized block-wise
     (tilemix_quantize_blocks: one scale per bq query / bk key tokens of a sequence) instead of
-    per token; with an INT8 cache the blocks apply to the cached K. With ``kv_int8`` the INT8 K/V cache is produced once at construction by the library's
-    own quantizer, and the fp16 K/V are dropped."""
+    per token (blocks of one token use the per-token pass; with ``fused_q`` the Q blocks must be one
+    token); with an INT8 cache the blocks apply to the cached K. When the K block is a multiple
+    of 64 keys, tilemix_prefill_fwd is told so (k_scale_block) and takes one K scale per key tile,
+    unless ``k_block_tiles`` is False. With ``kv_int8`` the INT8 K/V cache is produced once at
+    construction by the library's own quantizer, and the fp16 K/V are dropped."""
 
     def __init__(self, w, device: str = "cuda", out_dtype=torch.float32, with_lse: bool = True,
                  softmax_scale: float = 0.0, route_policy: Optional[tuple] = None,
-                 fused_q: bool = False, scale_blocks: Optional[tuple] = None):
-        if fused_q and scale_blocks is not None:
-            raise ValueError("fused Q quantization is per token; it does not take scale blocks")
+                 fused_q: bool = False, scale_blocks: Optional[tuple] = None,
+                 k_block_tiles: bool = True):
+        if fused_q and scale_blocks is not None and scale_blocks[0] != 1:
+            raise ValueError("fused Q quantization is per token; Q blocks must be 1 token with fused_q")
         self.w = w
         self.route_policy = route_policy
         self.fused_q = fused_q
         self.scale_blocks = scale_blocks
+        # block-wise K scales on 64-key multiples: the kernel takes one K scale per key tile
+        self.k_scale_block = (scale_blocks[1] if scale_blocks is not None and k_block_tiles
+                              and scale_blocks[1] % 64 == 0 else 0)
         dev = torch.device(device)
         T, hq, hk, d = w.total, w.hq, w.hk, w.d
         self.q = torch.from_numpy(w.q).to(dev)
@@ -76,12 +83,21 @@ class DeviceProblem:
 
     def quantize(self, stream=None):
         if self.scale_blocks is not None:
+            # blocks of one token are the per-token quantizer (same codes and scales): that pass,
+            # or for Q with fused_q the fused kernel itself
             bq, bk = self.scale_blocks
-            B.tilemix_quantize_blocks(self.q, self.q8, self.q_scale, self.cu, self.max_seqlen, bq,
-                                      stream=stream)
+            if not self.fused_q:
+                if bq == 1:
+                    B.tilemix_quantize_qk(q=self.q, q8=self.q8, q_scale=self.q_scale, stream=stream)
+                else:
+                    B.tilemix_quantize_blocks(self.q, self.q8, self.q_scale, self.cu, self.max_seqlen, bq,
+                                              stream=stream)
             if not self.w.kv_int8:
-                B.tilemix_quantize_blocks(self.k, self.k8, self.k_scale, self.cu, self.max_seqlen, bk,
-                                          stream=stream)
+                if bk == 1:
+                    B.tilemix_quantize_qk(k=self.k, k8=self.k8, k_scale=self.k_scale, stream=stream)
+                else:
+                    B.tilemix_quantize_blocks(self.k, self.k8, self.k_scale, self.cu, self.max_seqlen, bk,
+                                              stream=stream)
             return
         qargs = {} if self.fused_q else dict(q=self.q, q8=self.q8, q_scale=self.q_scale)
         if not self.w.kv_int8:
@@ -126,7 +142,7 @@ class DeviceProblem:
             softmax_scale=self.softmax_scale, out=self.out, lse=self.lse, workspace=self.workspace,
             debug_s32=debug_s32,
             debug_head=debug_head, debug_mtile_begin=debug_mtile_begin,
-            debug_mtile_count=debug_mtile_count, stream=stream)
+            debug_mtile_count=debug_mtile_count, k_scale_block=self.k_scale_block, stream=stream)
 
     def step(self, stream=None):
         self.quantize(stream)

@@ -109,6 +109,8 @@ BAD_CASES = [
                                setattr(p, "debug_ntiles_max", 2)), B.TILEMIX_EINVAL),
     ("debug ntiles", lambda p: (setattr(p, "debug_s32", FAKE), setattr(p, "debug_mtile_count", 1),
                                 setattr(p, "debug_ntiles_max", 1)), B.TILEMIX_EINVAL),
+    ("k_scale_block negative", lambda p: setattr(p, "k_scale_block", -64), B.TILEMIX_EINVAL),
+    ("k_scale_block not a tile multiple", lambda p: setattr(p, "k_scale_block", 96), B.TILEMIX_EINVAL),
 ]
 
 

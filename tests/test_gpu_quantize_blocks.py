@@ -105,3 +105,46 @@ def test_prefill_on_block_scales(name):
     assert n8 > 0
     err = np.abs(prob.out.cpu().numpy() - ref).max()
     assert err <= 2e-3, err
+
+
+BLOCK_TILE_CASES = {
+    # name: (workload factory, (bq, bk))
+    "varlen_bk128": (lambda: wl.custom([700, 129, 1000, 64], 8, 2, 128, bm_r=64, bn_r=128, group=1, seed=31),
+                     (1, 128)),
+    "bk64_d64": (lambda: wl.custom([513, 300], 4, 4, 64, bm_r=64, bn_r=128, group=2, seed=32), (64, 64)),
+    "kv_int8_bk256": (lambda: wl.custom([900, 300], 4, 2, 128, bm_r=128, bn_r=64, group=2, kv_int8=True,
+                                        seed=33), (128, 256)),
+    "zero_k_block": (lambda: _zero_k_block(), (1, 128)),
+}
+
+
+def _zero_k_block():
+    w = wl.custom([600], 4, 2, 128, bm_r=128, bn_r=128, route="int8", seed=34)
+    w.k[128:256] = 0  # one whole K block of zeros: its scale is 0, next to masked diagonal scores
+    return w
+
+
+@pytest.mark.parametrize("case", list(BLOCK_TILE_CASES))
+def test_prefill_block_scale_per_tile(case):
+    """With K scales constant over 64-key multiples the kernel takes one K scale per key tile
+    (k_scale_block); its outputs meet the 2e-3 bar against the oracle on the same block codes and
+    stay within rounding of the per-key path on the same inputs."""
+    make, (bq, bk) = BLOCK_TILE_CASES[case]
+    w = make()
+    tiles = runner.DeviceProblem(w, out_dtype=torch.float32, scale_blocks=(bq, bk))
+    assert tiles.k_scale_block == bk
+    per_key = runner.DeviceProblem(w, out_dtype=torch.float32, scale_blocks=(bq, bk), k_block_tiles=False)
+    assert per_key.k_scale_block == 0
+    for prob in (tiles, per_key):
+        prob.step()
+    torch.cuda.synchronize()
+    out_t, out_k = tiles.out.cpu().numpy(), per_key.out.cpu().numpy()
+    assert np.isfinite(out_t).all() and np.isfinite(tiles.lse.cpu().numpy()[np.isfinite(per_key.lse.cpu().numpy())]).all()
+    ref, _, n8, _ = oracle_blocks(w, bq, bk).prefill()
+    assert n8 > 0
+    assert np.abs(out_t - ref).max() <= 2e-3, case
+    assert np.abs(out_k - ref).max() <= 2e-3, case
+    # the two paths associate the three factors (integer score, K scale, per-row factor) in a
+    # different order; a last-bit difference in the exponent can flip the fp16 rounding of P,
+    # which moves an output by up to half an fp16 ulp of that P times |v|
+    assert np.abs(out_t - out_k).max() <= 5e-4, case
