@@ -668,7 +668,8 @@ def main():
         "quantize_pack_ms": round(pre_ms, 4),
         "quantize_gbps": round(q_bytes / (pre_ms * 1e-3) / 1e9, 1) if q_bytes else None,
         "roofline": {
-            "kernel": "prefill_fwd_kernel<128, false, false> (+ vt_pack pre-pass in the timed call)",
+            "kernel": f"prefill_fwd_kernel<{w.d}, {str(bool(w.kv_int8)).lower()}, false, "
+                      f"{str(prob.k_scale_block > 0).lower()}> (+ vt_pack pre-pass in the timed call)",
             "bound": "mfma",
             "achieved": round(fwd_tflops, 2),
             "peak": round(peak_mixed, 1),
