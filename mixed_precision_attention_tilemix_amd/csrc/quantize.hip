@@ -23,7 +23,9 @@ __device__ __forceinline__ uint64_t quantize8(const half8v v, float inv) {
 
 // One workgroup per (64 consecutive tokens, head): G = D/8 lanes per row, 256/G rows per pass,
 // four passes' loads in flight before any arithmetic. Token-major within a head keeps the
-// workgroup's scale stores in one contiguous 256-byte run.
+// workgroup's scale stores in one contiguous 256-byte run. Heads vary fastest over the
+// (one-dimensional) grid, so workgroups dispatched together read and write neighbouring rows of
+// the same tokens instead of one head's rows a whole token stride apart.
 template <int D>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const _Float16* __restrict__ x,
                                                             int64_t n_tok, int32_t n_head,
@@ -34,8 +36,8 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const _Float16* __re
   constexpr int RP = 256 / G;       // rows per pass
   constexpr int U = 64 / RP;        // passes: 64 tokens per workgroup
   const int g = threadIdx.x % G;
-  const int h = blockIdx.y;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 64 + threadIdx.x / G;
+  const int h = static_cast<int>(blockIdx.x % static_cast<uint32_t>(n_head));
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x / static_cast<uint32_t>(n_head)) * 64 + threadIdx.x / G;
 
   half8v v[U];
 #pragma unroll
@@ -73,10 +75,11 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(const _Float16* __
                                                               int8_t* __restrict__ x8,
                                                               float* __restrict__ scale) {
   constexpr int G = D / 8;  // 16-byte chunks per row
-  const int h = blockIdx.y, b = blockIdx.z;
+  // heads vary fastest over grid.x (neighbouring workgroups read neighbouring rows of the same tokens)
+  const int h = static_cast<int>(blockIdx.x % static_cast<uint32_t>(n_head)), b = blockIdx.y;
   const int64_t s0 = cu[b];
   const int64_t L = cu[b + 1] - s0;
-  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * block_rows;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x / static_cast<uint32_t>(n_head)) * block_rows;
   if (r0 >= L) return;  // uniform: past this sequence's tokens
   const int64_t nch = min(static_cast<int64_t>(block_rows), L - r0) * G;
   const _Float16* xb = x + (s0 + r0) * stride_tok + h * stride_head;
@@ -132,8 +135,9 @@ hipError_t launch_quantize_blocks(const void* x, int64_t n_tok, int32_t n_head, 
                                   int32_t max_seqlen, int32_t block_rows, int8_t* x8, float* scale,
                                   int32_t head_dim, hipStream_t stream) {
   if (n_tok == 0 || max_seqlen == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>((static_cast<int64_t>(max_seqlen) + block_rows - 1) / block_rows),
-                  static_cast<unsigned>(n_head), static_cast<unsigned>(batch));
+  const int64_t nblk = (static_cast<int64_t>(max_seqlen) + block_rows - 1) / block_rows * n_head;
+  if (nblk > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(nblk), static_cast<unsigned>(batch));
   const _Float16* xp = static_cast<const _Float16*>(x);
   if (head_dim == 128)
     quantize_blocks_kernel<128><<<grid, dim3(256), 0, stream>>>(xp, n_tok, n_head, stride_tok, stride_head,
@@ -149,7 +153,9 @@ hipError_t launch_quantize(const void* x, int64_t n_tok, int32_t n_head, int64_t
                            hipStream_t stream) {
   if (n_tok == 0 || n_head == 0) return hipSuccess;
   const _Float16* xp = static_cast<const _Float16*>(x);
-  const dim3 grid(static_cast<unsigned>((n_tok + 63) / 64), static_cast<unsigned>(n_head));
+  const int64_t nblk = (n_tok + 63) / 64 * n_head;
+  if (nblk > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(nblk));
   if (head_dim == 128)
     quantize_rows_kernel<128><<<grid, dim3(256), 0, stream>>>(xp, n_tok, n_head, stride_tok, stride_head, x8, scale);
   else
