@@ -235,6 +235,24 @@ tilemix_status tilemix_decode_workspace_size(const tilemix_fwd_params* params, i
 tilemix_status tilemix_decode_fwd(const tilemix_fwd_params* params, void* stream);
 
 /*
+ * tilemix_decode_fwd_noalloc - tilemix_decode_fwd for callers that cannot allocate device memory
+ * or pass a workspace: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation. Same definition, validation, kernels and results (bitwise) as tilemix_decode_fwd;
+ * the per-chunk partials live in a scratch array the library keeps on each GPU for the life of
+ * the process (tilemix_decode_noalloc_max_bytes() bytes), so params->workspace and
+ * params->workspace_bytes are ignored. The call allocates and frees nothing; on its first call on
+ * a device it looks up that device's scratch address. Every call on one GPU shares that GPU's
+ * scratch: calls that overlap in time on one GPU (other streams, other host threads) race.
+ * Nothing in the scratch needs clearing: each call writes every partial it reads.
+ * Errors: those of tilemix_decode_fwd, except the workspace checks; EINVAL when
+ * tilemix_decode_workspace_size() of these parameters exceeds the scratch size.
+ */
+tilemix_status tilemix_decode_fwd_noalloc(const tilemix_fwd_params* params, void* stream);
+
+/* Bytes of the per-device scratch of tilemix_decode_fwd_noalloc (32 MiB). */
+int64_t tilemix_decode_noalloc_max_bytes(void);
+
+/*
  * Routing policies on the device, fused with packing. The pages let the caller supply the routing
  * map R from any static or adaptive policy (Section 4.2, "Policy definition"; Limitations); these
  * calls compute R for one of two policies and write it straight into route words of the layout

@@ -25,7 +25,8 @@ TILEMIX_OK, TILEMIX_EINVAL, TILEMIX_EUNSUPPORTED, TILEMIX_ELAUNCH = 0, 1, 2, 3
 EXPORTED = ("tilemix_last_error", "tilemix_version", "tilemix_quantize_qk",
             "tilemix_pack_route_mask", "tilemix_prefill_workspace_size", "tilemix_prefill_fwd",
             "tilemix_decode_workspace_size", "tilemix_decode_fwd", "tilemix_route_workspace_size",
-            "tilemix_route_topk_maxabs", "tilemix_route_bernoulli", "tilemix_quantize_blocks")
+            "tilemix_route_topk_maxabs", "tilemix_route_bernoulli", "tilemix_quantize_blocks",
+            "tilemix_decode_fwd_noalloc", "tilemix_decode_noalloc_max_bytes")
 
 
 class TilemixError(RuntimeError):
@@ -118,6 +119,10 @@ def load(path: Optional[str] = None):
     L.tilemix_decode_workspace_size.argtypes = [ctypes.POINTER(FwdParams), ctypes.POINTER(ctypes.c_int64)]
     L.tilemix_decode_fwd.restype = ctypes.c_int
     L.tilemix_decode_fwd.argtypes = [ctypes.POINTER(FwdParams), vp]
+    L.tilemix_decode_fwd_noalloc.restype = ctypes.c_int
+    L.tilemix_decode_fwd_noalloc.argtypes = [ctypes.POINTER(FwdParams), vp]
+    L.tilemix_decode_noalloc_max_bytes.restype = i64
+    L.tilemix_decode_noalloc_max_bytes.argtypes = []
     for name in ("tilemix_route_topk_maxabs", "tilemix_route_bernoulli"):
         getattr(L, name).restype = ctypes.c_int
         getattr(L, name).argtypes = [ctypes.POINTER(RouteParams), vp]
@@ -299,6 +304,28 @@ def tilemix_decode_fwd(*, q, q8, q_scale, k8, k_scale, v8, v_scale, route_words,
                     v_scale=v_scale, causal=causal, softmax_scale=softmax_scale, lse=lse,
                     debug_s32=None, debug_head=0, debug_mtile_begin=0, debug_mtile_count=0)
     _check(load().tilemix_decode_fwd(ctypes.byref(p), _stream(stream)))
+
+
+def tilemix_decode_fwd_noalloc(*, q, q8, q_scale, k8, k_scale, v8, v_scale, route_words,
+                               cu_seqlens_q, cu_seqlens_k, cu_mtiles, max_seqlen_q: int,
+                               max_seqlen_k: int, route_block_m: int, route_block_n: int,
+                               route_group: int, out, causal: bool = True,
+                               softmax_scale: float = 0.0, lse=None, stream=None) -> None:
+    """tilemix_decode_fwd_noalloc: the decode call on the library's own per-device scratch (no
+    workspace argument)."""
+    p = _fwd_params(q=q, q8=q8, q_scale=q_scale, k8=k8, k_scale=k_scale, route_words=route_words,
+                    cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k, cu_mtiles=cu_mtiles,
+                    max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k,
+                    route_block_m=route_block_m, route_block_n=route_block_n,
+                    route_group=route_group, out=out, workspace=None, k=None, v=None, v8=v8,
+                    v_scale=v_scale, causal=causal, softmax_scale=softmax_scale, lse=lse,
+                    debug_s32=None, debug_head=0, debug_mtile_begin=0, debug_mtile_count=0)
+    _check(load().tilemix_decode_fwd_noalloc(ctypes.byref(p), _stream(stream)))
+
+
+def tilemix_decode_noalloc_max_bytes() -> int:
+    """Bytes of the per-device scratch of tilemix_decode_fwd_noalloc."""
+    return int(load().tilemix_decode_noalloc_max_bytes())
 
 
 def tilemix_route_workspace_size(*, batch: int, hkv: int, max_seqlen_k: int, route_block_n: int,

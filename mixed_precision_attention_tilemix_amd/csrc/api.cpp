@@ -242,6 +242,28 @@ tilemix::RouteArgs route_args(const tilemix_route_params* p, int64_t tmax) {
   return a;
 }
 
+// Checks shared by both decode entry points (everything except the workspace).
+tilemix_status check_decode(const tilemix_fwd_params* p, const char* what) {
+  if (tilemix_status st = check_params(p, what)) return st;
+  if (!p->kv_int8) return fail(TILEMIX_EUNSUPPORTED, "%s: reads an INT8 K/V cache (kv_int8 = 1)", what);
+  if (p->max_seqlen_q > 8)
+    return fail(TILEMIX_EUNSUPPORTED, "%s: max_seqlen_q %d > 8 (use tilemix_prefill_fwd)", what, p->max_seqlen_q);
+  if ((p->hq / p->hkv) * p->max_seqlen_q > tilemix::kDecodeMaxRows)
+    return fail(TILEMIX_EUNSUPPORTED, "%s: (hq / hkv) * max_seqlen_q = %d > %d query rows per KV head", what,
+                (p->hq / p->hkv) * p->max_seqlen_q, tilemix::kDecodeMaxRows);
+  if (p->debug_s32) return fail(TILEMIX_EINVAL, "%s: the debug dump is a prefill feature", what);
+  return TILEMIX_OK;
+}
+
+tilemix_status launch_decode_into(const tilemix_fwd_params* p, float* part, void* stream, const char* what) {
+  tilemix::DecodeArgs d{};
+  d.f = fwd_args(p);
+  d.part = part;
+  d.nchunk = static_cast<int32_t>(ceil_div(p->max_seqlen_k, tilemix::kDecodeChunk));
+  d.rmax = (p->hq / p->hkv) * p->max_seqlen_q;
+  return from_hip(tilemix::launch_decode(d, p->batch, p->head_dim, static_cast<hipStream_t>(stream)), what);
+}
+
 }  // namespace
 
 extern "C" {
@@ -372,28 +394,30 @@ tilemix_status tilemix_decode_workspace_size(const tilemix_fwd_params* p, int64_
 }
 
 tilemix_status tilemix_decode_fwd(const tilemix_fwd_params* p, void* stream) {
-  if (tilemix_status st = check_params(p, "decode_fwd")) return st;
-  if (!p->kv_int8)
-    return fail(TILEMIX_EUNSUPPORTED, "decode_fwd: reads an INT8 K/V cache (kv_int8 = 1)");
-  if (p->max_seqlen_q > 8)
-    return fail(TILEMIX_EUNSUPPORTED, "decode_fwd: max_seqlen_q %d > 8 (use tilemix_prefill_fwd)",
-                p->max_seqlen_q);
-  if ((p->hq / p->hkv) * p->max_seqlen_q > tilemix::kDecodeMaxRows)
-    return fail(TILEMIX_EUNSUPPORTED, "decode_fwd: (hq / hkv) * max_seqlen_q = %d > %d query rows per KV head",
-                (p->hq / p->hkv) * p->max_seqlen_q, tilemix::kDecodeMaxRows);
-  if (p->debug_s32) return fail(TILEMIX_EINVAL, "decode_fwd: the debug dump is a prefill feature");
+  if (tilemix_status st = check_decode(p, "decode_fwd")) return st;
   const int64_t need = decode_workspace(p);
   if (need > 0 && (p->workspace == nullptr || !aligned(p->workspace, 256) || p->workspace_bytes < need))
     return fail(TILEMIX_EINVAL, "decode_fwd: workspace must be 256-byte aligned and hold %lld bytes (got %lld)",
                 (long long)need, (long long)p->workspace_bytes);
   if (p->total_q == 0 || p->max_seqlen_q == 0) return ok();
-  tilemix::DecodeArgs d{};
-  d.f = fwd_args(p);
-  d.part = static_cast<float*>(p->workspace);
-  d.nchunk = static_cast<int32_t>(ceil_div(p->max_seqlen_k, tilemix::kDecodeChunk));
-  d.rmax = (p->hq / p->hkv) * p->max_seqlen_q;
-  return from_hip(tilemix::launch_decode(d, p->batch, p->head_dim, static_cast<hipStream_t>(stream)),
-                  "decode_fwd");
+  return launch_decode_into(p, static_cast<float*>(p->workspace), stream, "decode_fwd");
+}
+
+int64_t tilemix_decode_noalloc_max_bytes(void) { return tilemix::kDecodeScratchBytes; }
+
+tilemix_status tilemix_decode_fwd_noalloc(const tilemix_fwd_params* p, void* stream) {
+  if (tilemix_status st = check_decode(p, "decode_fwd_noalloc")) return st;
+  const int64_t need = decode_workspace(p);
+  if (need > tilemix::kDecodeScratchBytes)
+    return fail(TILEMIX_EINVAL,
+                "decode_fwd_noalloc: these shapes need %lld bytes of decode scratch, more than the library's "
+                "%lld (use tilemix_decode_fwd with a workspace)",
+                (long long)need, (long long)tilemix::kDecodeScratchBytes);
+  if (p->total_q == 0 || p->max_seqlen_q == 0) return ok();
+  float* part = nullptr;
+  if (hipError_t e = tilemix::decode_scratch(&part); e != hipSuccess)
+    return from_hip(e, "decode_fwd_noalloc (scratch address)");
+  return launch_decode_into(p, part, stream, "decode_fwd_noalloc");
 }
 
 tilemix_status tilemix_route_workspace_size(const tilemix_route_params* p, int64_t* bytes) {

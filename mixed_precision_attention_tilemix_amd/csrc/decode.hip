@@ -22,10 +22,39 @@
 // tokens, fewer than a route tile's rows, so every row of a sequence reads route row
 // cu_mtiles[b], and the 32 keys of a tile lie in one key tile: the INT8 / FP16 choice is uniform
 // per wavefront.
+#include <mutex>
+
 #include "device_types.h"
 #include "launch.h"
 
 namespace tilemix {
+
+// Scratch of the allocation-free decode entry point: the per-chunk (max, sum, O) partials of a
+// call, in the layout of the caller workspace of tilemix_decode_fwd. Every GPU the library runs on
+// holds its own copy until the process ends; calls on one GPU share it (and race if they overlap).
+// Host code never passes this name to a kernel: on the host it is a stand-in, not a device
+// address; decode_scratch() returns the address of the current device's copy.
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(float** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {  // once per device, with that device current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = static_cast<float*>(addr[dev]);
+  return hipSuccess;
+}
+
 namespace {
 
 constexpr int CH = kDecodeChunk;      // keys per chunk workgroup

@@ -83,6 +83,14 @@ struct DecodeArgs {
 // Chunk pass then merge pass, both on `stream`.
 hipError_t launch_decode(const DecodeArgs& a, int32_t batch, int32_t head_dim, hipStream_t stream);
 
+// Bytes of the library's own per-device decode scratch (the allocation-free decode entry point
+// keeps the per-chunk partials there instead of in a caller workspace).
+constexpr int64_t kDecodeScratchBytes = int64_t{32} << 20;
+
+// Device address of that scratch on the current device: looked up once per device with the
+// device current, then cached. Allocates nothing.
+hipError_t decode_scratch(float** ptr);
+
 // Routing policies fused with packing. Groups per sequence are at most kRouteMaxGroups for the
 // top-k policy (its select pass ranks them in LDS).
 constexpr int kRouteMaxGroups = 8192;

@@ -212,6 +212,32 @@ def test_decode_validation(lib, name, mutate, status):
 
 def test_decode_null_params(lib):
     assert lib.tilemix_decode_fwd(None, None) == B.TILEMIX_EINVAL
+    assert lib.tilemix_decode_fwd_noalloc(None, None) == B.TILEMIX_EINVAL
+
+
+# the allocation-free decode call validates everything tilemix_decode_fwd does except the workspace
+NOALLOC_BAD_CASES = [c for c in DECODE_BAD_CASES if "workspace" not in c[0]]
+
+
+@pytest.mark.parametrize("name,mutate,status", NOALLOC_BAD_CASES, ids=[c[0] for c in NOALLOC_BAD_CASES])
+def test_decode_noalloc_validation(lib, name, mutate, status):
+    p = decode_params()
+    mutate(p)
+    got = lib.tilemix_decode_fwd_noalloc(ctypes.byref(p), None)
+    assert got == status, (name, B.last_error())
+    assert B.last_error().startswith("decode_fwd_noalloc")
+
+
+def test_decode_noalloc_rejects_more_than_its_scratch(lib):
+    cap = lib.tilemix_decode_noalloc_max_bytes()
+    assert cap == 32 << 20
+    p = decode_params()
+    p.batch = 8000  # 8000 x 2 KV heads x 4 chunks x 2 rows x 132 fp32 = 67.6 MB of partials
+    n = ctypes.c_int64(0)
+    assert lib.tilemix_decode_workspace_size(ctypes.byref(p), ctypes.byref(n)) == B.TILEMIX_OK
+    assert n.value > cap
+    assert lib.tilemix_decode_fwd_noalloc(ctypes.byref(p), None) == B.TILEMIX_EINVAL
+    assert "scratch" in B.last_error()
 
 
 def test_decode_workspace_size(lib):
