@@ -164,6 +164,21 @@ typedef struct tilemix_fwd_params {
    * its first key) instead of one per key. Any other k_scale content with a nonzero value is
    * undefined. tilemix_decode_fwd ignores it. */
   int32_t k_scale_block;
+
+  /* Nonzero: a single-buffered debug instance of tilemix_prefill_fwd. It loads each key tile
+   * into the one LDS stage and waits for the loads before any wavefront computes on it, where the
+   * production kernel streams tile n+1 into a second stage while tile n is computed. Its O, LSE
+   * equal the production kernel's bit for bit; a difference means a staging race. Slower. At most
+   * one of debug_s32, debug_sync_stages and state_fp16 may be set (else TILEMIX_EINVAL);
+   * tilemix_decode_fwd rejects it (TILEMIX_EINVAL). */
+  int32_t debug_sync_stages;
+
+  /* Nonzero: the FP16-state variant (the TileMix page, Section 4.3 and Appendix G.3): the
+   * online-softmax state kept between key tiles (running row max, row sum, output accumulator)
+   * is rounded to binary16 after every 64-key tile; scores, P and the accumulation inside a tile
+   * stay as without it. The row max is held in log2 units, so |max score| * log2(e) must stay
+   * below 65504. 0 keeps fp32 state. Prefill only: tilemix_decode_fwd rejects it. */
+  int32_t state_fp16;
 } tilemix_fwd_params;
 
 /*

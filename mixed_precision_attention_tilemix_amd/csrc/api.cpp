@@ -58,7 +58,7 @@ tilemix_status check_quant_group(const char* name, const void* x, int64_t n, int
 struct WorkspaceLayout {
   int64_t vt_tiles;   // V^T tile slots per KV head
   int64_t vt_bytes;   // bytes of the V^T region
-  int64_t ks_off;     // byte offset of the per-key score factors
+  int64_t ks_off;     // byte offset of the per-key K scales (one fp32 per key of every tile)
   int64_t k16_off;    // byte offset of the fp16 K copy (INT8 cache only)
   int64_t total;      // bytes in all
 };
@@ -70,7 +70,7 @@ WorkspaceLayout workspace_layout(const tilemix_fwd_params* p) {
   w.vt_tiles = tilemix::key_tiles_bound(p->total_k, p->batch);
   w.vt_bytes = round_up(static_cast<int64_t>(p->hkv) * w.vt_tiles * tilemix::kKeyTile * p->head_dim * 2, 256);
   w.ks_off = w.vt_bytes;
-  w.k16_off = w.ks_off + round_up(static_cast<int64_t>(p->hkv) * w.vt_tiles * 2 * tilemix::kKeyTile * 4, 256);
+  w.k16_off = w.ks_off + round_up(static_cast<int64_t>(p->hkv) * w.vt_tiles * tilemix::kKeyTile * 4, 256);
   w.total = w.k16_off + (p->kv_int8 ? round_up(p->total_k * p->hkv * p->head_dim * 2, 256) : 0);
   return w;
 }
@@ -128,6 +128,8 @@ tilemix::FwdArgs fwd_args(const tilemix_fwd_params* p) {
   a.dump_mcount = p->debug_mtile_count;
   a.dump_ntiles = p->debug_ntiles_max;
   a.k_block = p->k_scale_block;
+  a.sync_stages = p->debug_sync_stages != 0;
+  a.state_fp16 = p->state_fp16 != 0;
   return a;
 }
 
@@ -252,6 +254,8 @@ tilemix_status check_decode(const tilemix_fwd_params* p, const char* what) {
     return fail(TILEMIX_EUNSUPPORTED, "%s: (hq / hkv) * max_seqlen_q = %d > %d query rows per KV head", what,
                 (p->hq / p->hkv) * p->max_seqlen_q, tilemix::kDecodeMaxRows);
   if (p->debug_s32) return fail(TILEMIX_EINVAL, "%s: the debug dump is a prefill feature", what);
+  if (p->debug_sync_stages || p->state_fp16)
+    return fail(TILEMIX_EINVAL, "%s: debug_sync_stages and state_fp16 are prefill features", what);
   return TILEMIX_OK;
 }
 
@@ -354,6 +358,8 @@ tilemix_status tilemix_prefill_fwd(const tilemix_fwd_params* p, void* stream) {
       return fail(TILEMIX_EINVAL, "prefill_fwd: debug_ntiles_max %d < ceil(max_seqlen_k / route_block_n)",
                   p->debug_ntiles_max);
   }
+  if ((p->debug_s32 != nullptr) + (p->debug_sync_stages != 0) + (p->state_fp16 != 0) > 1)
+    return fail(TILEMIX_EINVAL, "prefill_fwd: at most one of debug_s32, debug_sync_stages, state_fp16");
   if (p->k_scale_block < 0 || p->k_scale_block % tilemix::kKeyTile)
     return fail(TILEMIX_EINVAL, "prefill_fwd: k_scale_block %d is not 0 or a multiple of %d", p->k_scale_block,
                 tilemix::kKeyTile);

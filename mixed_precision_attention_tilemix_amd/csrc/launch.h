@@ -55,10 +55,12 @@ struct FwdArgs {
   _Float16* vt_ws;        // [hkv][vt_tiles][D][64] swizzled V^T tiles
   const _Float16* vt;     // the same, read-only view
   int64_t vt_tiles;       // tile slots per KV head (>= tiles of all sequences)
-  float* ks_ws;           // [hkv][vt_tiles][2][64] per-key score factors dk' and -1.5*2^23*dk'
+  float* ks_ws;           // [hkv][vt_tiles][64] k_scale of every key of a tile (the last key's past the end)
   const float* ks;        // the same, read-only view
   _Float16* k16_ws;       // INT8 cache only: exact fp16(k8) [total_k, hkv, D]
   int32_t k_block;        // > 0: K scales constant over 64-key tiles (one factor per tile)
+  int32_t sync_stages;    // debug instance: every staging load waited for before any compute
+  int32_t state_fp16;     // online-softmax state (m, l, O) rounded to binary16 after every key tile
 };
 
 // V^T tiles (and, with an INT8 cache, fp16 K) into the workspace; must precede launch_prefill.

@@ -42,12 +42,10 @@
 //   per lane half until the epilogue.
 //
 // INT8 scores
-//   The int32 accumulator is converted to fp32 and multiplied by the per-key factor dk' of the
-//   V^T pre-pass, then one FMA with the per-row factor and the running max gives the exponent.
-//   The factors reach the multiply through a DPP row broadcast: each lane loads one factor per
-//   32-key half and accumulator slot t takes it from lane t of its 16-lane row.
-//   (The pre-pass also stores offsets for a form that starts the accumulator at the bit pattern
-//   of 1.5 * 2^23 and rescales with one FMA; it saves the conversion but measured slower.)
+//   The int32 accumulator is converted to fp32 and multiplied by the key's k_scale (gathered per
+//   tile by the V^T pre-pass), then one FMA with the per-row factor and the running max gives
+//   the exponent. The scales reach the multiply through a DPP row broadcast: each lane loads one
+//   scale per 32-key half and accumulator slot t takes it from lane t of its 16-lane row.
 #include <utility>
 
 #include "device_types.h"
@@ -80,7 +78,7 @@ struct Smem {
   static constexpr int VBUF = KBUF + 2 * KSTAGE;  // two V^T stages, [D][BN] fp16 as vt_pack.hip
   static constexpr int VSTAGE = D * BN * 2;
   static constexpr int SBUF = VBUF + 2 * VSTAGE;  // two slots of per-key factors
-  static constexpr int SSLOT = 2 * BN * 4;        // dk'[BN], bk[BN]
+  static constexpr int SSLOT = BN * 4;            // k_scale of the tile's keys
   static constexpr int BYTES = SBUF + 2 * SSLOT;
   // The 16 lanes served together read 16 different rows at one chunk index: XOR-ing the chunk
   // with (row / rows-per-256-bytes) puts them on 16 distinct 16-byte bank groups.
@@ -164,7 +162,7 @@ struct Stager {
     k16 = reinterpret_cast<const char*>(a.k) + k_begin * st16 + hk * a.k_stride_head * 2;
     k8 = reinterpret_cast<const char*>(a.k8) + static_cast<int64_t>(k_begin) * st8 + static_cast<int64_t>(hk) * D;
     vt = reinterpret_cast<const char*>(a.vt + tile0 * (D * BN));
-    ks = reinterpret_cast<const char*>(a.ks + tile0 * (2 * BN));
+    ks = reinterpret_cast<const char*>(a.ks + tile0 * BN);
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < I16; ++i) o16[i] = off16(lane, i, BN);
@@ -226,10 +224,10 @@ struct Stager {
     vt += D * BN * 2;
   }
 
-  // The 512 bytes of per-key factors of the next factor tile into a factor slot.
+  // The 256 bytes of per-key K scales of the next tile into a factor slot.
   __device__ __forceinline__ void s_next(char* buf) {
-    if (w == NW - 1 && (threadIdx.x & 63) < 32) dma16(ks, ov, buf);
-    ks += 2 * BN * 4;
+    if (w == NW - 1 && (threadIdx.x & 63) < 16) dma16(ks, ov, buf);
+    ks += BN * 4;
   }
 };
 
@@ -347,7 +345,7 @@ struct Wave {
       }
   }
 
-  // The per-key factor dk' of key half KB that this lane's 16-lane row broadcasts: lane i of a
+  // The per-key K scale of key half KB that this lane's 16-lane row broadcasts: lane i of a
   // row holds the factor of accumulator slot i of the row's lanes (key 16 (i / 8) + 8 hl + i % 8
   // of the half), so slot t reads it from lane t of its own row (DPP row_newbcast), and one
   // 4-byte LDS read per lane replaces the sixteen factors each lane would otherwise load.
@@ -358,7 +356,7 @@ struct Wave {
   }
 
   // Raw scores of half KB -> fp32 scores in units of 1 / c[KB], with the half's per-key factors
-  // broadcast from fr. INT8: dk' * (q8 . k8); FP16: the dot product (times dk' for an INT8 cache).
+  // broadcast from fr. INT8: k_scale * (q8 . k8); FP16: the dot product (times k_scale for an INT8 cache).
   template <int KB, bool I8>
   __device__ __forceinline__ void convert_f(float fr) {
     if constexpr (KBLK) {
@@ -415,12 +413,23 @@ struct Wave {
 
   // Both halves of a tile after their softmax (P of each half against m_use): one slow-path
   // check for the tile; the slow path raises the max over both halves and recomputes both P.
+  // EXACT (the FP16-state instance): the max is raised whenever a score exceeds it, as in the
+  // plain online recurrence, so that P <= 1 and the row sum stays within binary16 range.
+  template <bool EXACT>
   __device__ __forceinline__ void settle_tile(float rs0, float rs1) {
-    if (__any(row_valid && (!(rs0 + rs1 <= P_LIMIT) || m == -INFINITY))) {
-      float mx = -INFINITY;
+    float mx = -INFINITY;
+    if constexpr (EXACT) {
 #pragma unroll
       for (int t = 0; t < 16; ++t) mx = fmaxf(mx, fmaxf(s[0][t] * c[0], s[1][t] * c[1]));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = static_cast<float>(static_cast<_Float16>(mx));  // the max is state: binary16
+    }
+    if (__any(row_valid && (EXACT ? mx > m : (!(rs0 + rs1 <= P_LIMIT) || m == -INFINITY)))) {
+      if constexpr (!EXACT) {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) mx = fmaxf(mx, fmaxf(s[0][t] * c[0], s[1][t] * c[1]));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+      }
       if (mx > m) {
         const float alpha = fast_exp2(m - mx);
 #pragma unroll
@@ -435,6 +444,16 @@ struct Wave {
     l += rs0 + rs1;
   }
 
+  // The state kept between tiles rounded to binary16 (round to nearest even) and widened back:
+  // this lane's part of the row sum and O (the running max is rounded where it is raised, before
+  // P and the rescale factor are computed from it).
+  __device__ __forceinline__ void round_state_fp16() {
+    l = static_cast<float>(static_cast<_Float16>(l));
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+      for (int t = 0; t < 16; ++t) o[i][t] = static_cast<float>(static_cast<_Float16>(o[i][t]));
+  }
 };
 
 // Where the debug dump of the current tiles goes (DUMP instances only).
@@ -486,8 +505,22 @@ __device__ __forceinline__ float quantize_q_half(const char* q16, int row, int h
   return s;
 }
 
-template <int D, bool KV8, bool DUMP, bool KBLK>
+// Instances of the fused kernel. Production streams tile n+1 into the second stage while tile n
+// is computed. The others are debug and numerics instances:
+//   kDump  writes the raw INT8 accumulators of every computed INT8-routed tile;
+//   kKblk  takes one K scale per 64-key tile (block-wise K scales);
+//   kSync  single-buffered: loads tile n into the one stage, waits, then computes it; its
+//          results must equal the production instance's bit for bit (a staging race would show
+//          as a difference);
+//   kF16s  rounds the online-softmax state (m, l and O) to binary16 after every 64-key tile.
+enum Variant : int { kProd = 0, kDump = 1, kKblk = 2, kSync = 3, kF16s = 4 };
+
+template <int D, bool KV8, int VAR>
 __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a) {
+  constexpr bool DUMP = VAR == kDump;
+  constexpr bool KBLK = VAR == kKblk;
+  constexpr bool SYNC = VAR == kSync;
+  constexpr bool F16S = VAR == kF16s;
   using L = Smem<D>;
   __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
 
@@ -610,8 +643,9 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
       wv.cq = fmaxf(quantize_q_half<D>(q16w, ROWS_W * w + r32, hl, wv.q8f) * a.scale_log2, 1e-30f);
   }
 
-  // ---- prologue: K, V^T and factors of tile 0
-  if (n_tiles > 0) {
+  // ---- prologue: K, V^T and factors of tile 0 (the single-buffered instance loads every tile in
+  // its own iteration)
+  if (!SYNC && n_tiles > 0) {
     stg.k_next(kbuf, rb0 != full, rb0 != 0u);
     stg.v_next(vbuf);
     stg.s_next(sbuf);
@@ -621,7 +655,12 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
   // the direct loads of tile n+1 fly
   for (int n = 0; n < n_tiles; ++n) {
     dma_barrier();  // tile n landed; the stages of tile n-1 are free
-    if (n + 1 < n_tiles) {
+    if constexpr (SYNC) {
+      stg.k_next(kbuf, rb0 != full, rb0 != 0u);
+      stg.v_next(vbuf);
+      stg.s_next(sbuf);
+      dma_barrier();
+    } else if (n + 1 < n_tiles) {
       stg.k_next(kbuf + ((n + 1) & 1) * L::KSTAGE, rb1 != full, rb1 != 0u);
       stg.v_next(vbuf + ((n + 1) & 1) * L::VSTAGE);
       stg.s_next(sbuf + ((n + 1) & 1) * L::SSLOT);
@@ -629,9 +668,10 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
     if (wave_live) {
       const int j0 = n * BN;
       const bool i8 = (rb0 >> my_rl) & 1u;
-      const char* kst = kbuf + (n & 1) * L::KSTAGE;
-      const char* vst = vbuf + (n & 1) * L::VSTAGE;
-      const float* scl = reinterpret_cast<const float*>(sbuf + (n & 1) * L::SSLOT);
+      const int st = SYNC ? 0 : (n & 1);
+      const char* kst = kbuf + st * L::KSTAGE;
+      const char* vst = vbuf + st * L::VSTAGE;
+      const float* scl = reinterpret_cast<const float*>(sbuf + st * L::SSLOT);
       if (i8) {
         wv.qk_i8(kst);
         if constexpr (DUMP) wv.dump_i8(j0 <= dc.act_limit ? dc.row : nullptr, j0, dc.Lk, dc.bn_r, dc.tile_stride);
@@ -655,7 +695,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
       }
       const float rs0 = wv.template softmax<0>();
       const float rs1 = wv.template softmax<1>();
-      wv.settle_tile(rs0, rs1);
+      wv.template settle_tile<F16S>(rs0, rs1);
       half8v vf1[2][D / 32];
       wv.template load_v<1>(vst, vf1);
       wv.template pv_regs<0>(vf0);
@@ -663,6 +703,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
       // the second half's V^T reads first, then all P.V MFMAs
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 32), 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 4 * (D / 32), 0);
+      if constexpr (F16S) wv.round_state_fp16();
     }
     rb0 = rb1;
     // tile n+2's position in its routing group, kept as a counter (no division per tile)
@@ -713,12 +754,17 @@ hipError_t launch_t(const FwdArgs& a, int32_t batch, hipStream_t stream) {
   dim3 grid(static_cast<unsigned>(a.hq), static_cast<unsigned>(n_ct), static_cast<unsigned>(batch));
   // the debug dump of the INT8 accumulators is compiled into a separate instance of the kernel
   // (with the dump the per-key instance runs: block-wise scales are per-key scales too)
+  // (the per-key instances also serve block-wise K scales: each key's scale is its block's)
   if (a.dump != nullptr)
-    prefill_fwd_kernel<D, KV8, true, false><<<grid, dim3(NW * 64), 0, stream>>>(a);
+    prefill_fwd_kernel<D, KV8, kDump><<<grid, dim3(NW * 64), 0, stream>>>(a);
+  else if (a.sync_stages)
+    prefill_fwd_kernel<D, KV8, kSync><<<grid, dim3(NW * 64), 0, stream>>>(a);
+  else if (a.state_fp16)
+    prefill_fwd_kernel<D, KV8, kF16s><<<grid, dim3(NW * 64), 0, stream>>>(a);
   else if (a.k_block > 0)
-    prefill_fwd_kernel<D, KV8, false, true><<<grid, dim3(NW * 64), 0, stream>>>(a);
+    prefill_fwd_kernel<D, KV8, kKblk><<<grid, dim3(NW * 64), 0, stream>>>(a);
   else
-    prefill_fwd_kernel<D, KV8, false, false><<<grid, dim3(NW * 64), 0, stream>>>(a);
+    prefill_fwd_kernel<D, KV8, kProd><<<grid, dim3(NW * 64), 0, stream>>>(a);
   return hipGetLastError();
 }
 

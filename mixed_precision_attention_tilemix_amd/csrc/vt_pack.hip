@@ -4,12 +4,9 @@
 // With an INT8 K/V cache the same pass dequantizes V (fp16(v_scale * v8)) and widens K8 to an
 // exact fp16 copy for the FP16-routed tiles. HBM-bound: one read and one write of V (and K).
 //
-// The same pass stores, per key, the two factors the fused kernel uses to turn an INT8 dot
-// product into a score with one fused multiply-add. The kernel's integer accumulator starts at
-// the bit pattern of 1.5 * 2^23, so that (since |q8 . k8| <= 127 * 127 * 128 < 2^22) it reads
-// as the fp32 number F = 1.5 * 2^23 + q8 . k8 exactly. With dk' = k_scale rounded to 22
-// significant bits, bk = -1.5 * 2^23 * dk' is exact, and fma(F, dk', bk) = round(dk' * q8 . k8).
-// dk' differs from k_scale by less than 2^-22 relative.
+// The same pass gathers the k_scale of every key of the tile into one 256-byte block (keys past
+// the sequence end repeat the last key's), which the fused kernel fetches with one direct load
+// per tile and multiplies into the converted INT8 dot products.
 #include "device_types.h"
 #include "launch.h"
 #include "tile_layout.h"
@@ -61,11 +58,7 @@ __global__ __launch_bounds__(256) void vt_pack_kernel(const FwdArgs a) {
   const int64_t slot = static_cast<int64_t>(hk) * a.vt_tiles + key_tiles_before(a.cu_k, b) + n;
   if (tid < T) {
     const int64_t tk = k_begin + min(j0 + tid, Lk - 1);
-    const float ks = a.k_scale[static_cast<int64_t>(hk) * a.total_k + tk];
-    const uint32_t bits = (__builtin_bit_cast(uint32_t, ks) + 2u) & ~3u;  // 22 significant bits
-    const float dk = __builtin_bit_cast(float, bits);
-    a.ks_ws[slot * (2 * T) + tid] = dk;
-    a.ks_ws[slot * (2 * T) + T + tid] = -12582912.0f * dk;
+    a.ks_ws[slot * T + tid] = a.k_scale[static_cast<int64_t>(hk) * a.total_k + tk];
   }
   _Float16* out = a.vt_ws + slot * (D * T);
   for (int ch = tid; ch < D * (T / 8); ch += 256) {

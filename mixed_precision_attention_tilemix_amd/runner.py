@@ -130,7 +130,8 @@ class DeviceProblem:
             raise ValueError(f"unknown route policy {pol[0]!r}")
 
     def attention(self, stream=None, debug_s32: Optional[torch.Tensor] = None, debug_head: int = 0,
-                  debug_mtile_begin: int = 0, debug_mtile_count: int = 0):
+                  debug_mtile_begin: int = 0, debug_mtile_count: int = 0,
+                  debug_sync_stages: bool = False, state_fp16: bool = False):
         w = self.w
         B.tilemix_prefill_fwd(
             q=self.q, k=self.k, v=self.v, q8=None if self.fused_q else self.q8,
@@ -142,7 +143,8 @@ class DeviceProblem:
             softmax_scale=self.softmax_scale, out=self.out, lse=self.lse, workspace=self.workspace,
             debug_s32=debug_s32,
             debug_head=debug_head, debug_mtile_begin=debug_mtile_begin,
-            debug_mtile_count=debug_mtile_count, k_scale_block=self.k_scale_block, stream=stream)
+            debug_mtile_count=debug_mtile_count, k_scale_block=self.k_scale_block,
+            debug_sync_stages=debug_sync_stages, state_fp16=state_fp16, stream=stream)
 
     def step(self, stream=None):
         self.quantize(stream)

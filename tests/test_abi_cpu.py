@@ -109,6 +109,14 @@ BAD_CASES = [
                                setattr(p, "debug_ntiles_max", 2)), B.TILEMIX_EINVAL),
     ("debug ntiles", lambda p: (setattr(p, "debug_s32", FAKE), setattr(p, "debug_mtile_count", 1),
                                 setattr(p, "debug_ntiles_max", 1)), B.TILEMIX_EINVAL),
+    ("sync with state_fp16", lambda p: (setattr(p, "debug_sync_stages", 1), setattr(p, "state_fp16", 1)),
+     B.TILEMIX_EINVAL),
+    ("dump with sync", lambda p: (setattr(p, "debug_s32", FAKE), setattr(p, "debug_mtile_count", 1),
+                                  setattr(p, "debug_ntiles_max", 2), setattr(p, "debug_sync_stages", 1)),
+     B.TILEMIX_EINVAL),
+    ("dump with state_fp16", lambda p: (setattr(p, "debug_s32", FAKE), setattr(p, "debug_mtile_count", 1),
+                                        setattr(p, "debug_ntiles_max", 2), setattr(p, "state_fp16", 1)),
+     B.TILEMIX_EINVAL),
     ("k_scale_block negative", lambda p: setattr(p, "k_scale_block", -64), B.TILEMIX_EINVAL),
     ("k_scale_block not a tile multiple", lambda p: setattr(p, "k_scale_block", 96), B.TILEMIX_EINVAL),
 ]
@@ -155,13 +163,13 @@ def test_workspace_size(lib):
     p = base_params()
     n = ctypes.c_int64(0)
     assert lib.tilemix_prefill_workspace_size(ctypes.byref(p), ctypes.byref(n)) == B.TILEMIX_OK
-    # hkv * (ceil(total_k / 64) + batch) tiles, each 64 x head_dim fp16 of V^T and 2 x 64 fp32
-    # per-key score factors
+    # hkv * (ceil(total_k / 64) + batch) tiles, each 64 x head_dim fp16 of V^T and the 64 fp32
+    # K scales of its keys
     tiles = 2 * (256 // 64 + 1)
-    assert n.value == tiles * 64 * 128 * 2 + tiles * 2 * 64 * 4
+    assert n.value == tiles * 64 * 128 * 2 + tiles * 64 * 4
     p.kv_int8 = 1
     assert lib.tilemix_prefill_workspace_size(ctypes.byref(p), ctypes.byref(n)) == B.TILEMIX_OK
-    assert n.value == tiles * 64 * 128 * 2 + tiles * 2 * 64 * 4 + 256 * 2 * 128 * 2
+    assert n.value == tiles * 64 * 128 * 2 + tiles * 64 * 4 + 256 * 2 * 128 * 2
     p.head_dim = 80
     assert lib.tilemix_prefill_workspace_size(ctypes.byref(p), ctypes.byref(n)) == B.TILEMIX_EUNSUPPORTED
     assert lib.tilemix_prefill_workspace_size(None, ctypes.byref(n)) == B.TILEMIX_EINVAL
@@ -193,6 +201,8 @@ DECODE_BAD_CASES = [
     ("too many rows", lambda p: (setattr(p, "hq", 16), setattr(p, "hkv", 2), setattr(p, "max_seqlen_q", 4)),
      B.TILEMIX_EUNSUPPORTED),
     ("debug dump", lambda p: setattr(p, "debug_s32", FAKE), B.TILEMIX_EINVAL),
+    ("sync stages", lambda p: setattr(p, "debug_sync_stages", 1), B.TILEMIX_EINVAL),
+    ("fp16 state", lambda p: setattr(p, "state_fp16", 1), B.TILEMIX_EINVAL),
     ("head_dim", lambda p: setattr(p, "head_dim", 96), B.TILEMIX_EUNSUPPORTED),
     ("null workspace", lambda p: setattr(p, "workspace", None), B.TILEMIX_EINVAL),
     ("small workspace", lambda p: setattr(p, "workspace_bytes", 1024), B.TILEMIX_EINVAL),

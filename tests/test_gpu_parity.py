@@ -189,8 +189,8 @@ def test_outlier_channels_and_scale_override():
 @pytest.mark.parametrize("route", [None, "fp16", "int8"])
 def test_rising_scores_rescale_paths(route):
     """Key norms grow along the sequence, so the running max keeps rising and the lazy-rescale slow
-    path fires in the middle of the key loop, including while the P of the previous key half is
-    still pending (route changes and FP16 runs take the generic iteration)."""
+    path fires in the middle of the key loop, on INT8- and FP16-routed tiles and across route
+    changes."""
     w = wl.custom(seqlens=[1100, 700], hq=4, hk=2, d=128, bm_r=128, bn_r=128, group=1, seed=31,
                   route=route, p_fp16=0.5)
     growth = (1.0 + np.arange(w.total, dtype=np.float32) / 96.0)[:, None, None]
@@ -262,8 +262,8 @@ def test_deterministic():
 @pytest.mark.parametrize("name", ["varlen64k", "mha8k"])
 def test_deterministic_full_size(name):
     """Bitwise identical outputs run to run, for the production kernel and for the instance with
-    the debug dump compiled in (which takes the generic iteration everywhere): the staged K/V
-    tiles must have landed in LDS before any wave reads them."""
+    the debug dump compiled in: the staged K/V tiles must have landed in LDS before any wave
+    reads them."""
     w = named(name)
     prob = DeviceProblem(w)
     runs = []
