@@ -56,6 +56,85 @@ PAGES_CONTEXT = {
 }
 
 
+def prefill_metric(w):
+    """The metric string of a prefill workload, built from its shape (the 32k GQA workload gives
+    the headline metric)."""
+    def tokens(n):
+        return f"{n // 1024}k" if n % 1024 == 0 else str(n)
+    if w.batch == 1:
+        where = f"L={tokens(w.seqlens[0])}"
+    else:
+        where = f"a varlen batch of {w.batch} sequences ({tokens(w.total) if w.total % 1024 == 0 else w.total} tokens)"
+    kind = "MHA" if w.hq == w.hk else "GQA"
+    extra = ", INT8 K/V cache" if w.kv_int8 else ""
+    causal = "causal" if w.causal else "non-causal"
+    return f"{causal} prefill attention TFLOPS & % MFMA roofline at {where}, d={w.d}, {kind}{extra}"
+
+
+def measure_mfma_peaks(stream, blocks=4096, iters=2048, reps=5):
+    """Dense MFMA rates this GPU reaches on the two shapes the fused kernel issues
+    (libtilemix_peak.so: long runs of independent 32x32 MFMAs, nothing else in the loop). Returns
+    {"int8": TOP/s, "fp16": TFLOP/s}, the best of `reps` timed launches each."""
+    import ctypes
+    import torch
+    from mixed_precision_attention_tilemix_amd import build as pkg_build
+    if not os.path.exists(pkg_build.PEAK_LIB):
+        raise FileNotFoundError(f"{pkg_build.PEAK_LIB} is missing: build it with "
+                                "python -m mixed_precision_attention_tilemix_amd.build")
+    lib = ctypes.CDLL(pkg_build.PEAK_LIB)
+    lib.tilemix_peak_mfma.restype = ctypes.c_int
+    lib.tilemix_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    chains = lib.tilemix_peak_chains()
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    res = {}
+    for kind, name, flops_per in ((0, "int8", 2 * 32 * 32 * 32), (1, "fp16", 2 * 32 * 32 * 16)):
+        def launch():
+            st = lib.tilemix_peak_mfma(kind, blocks, iters, ctypes.c_void_p(out.data_ptr()),
+                                       ctypes.c_void_p(stream.cuda_stream))
+            if st != 0:
+                raise RuntimeError(f"tilemix_peak_mfma failed: {st}")
+        launch()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        total = blocks * 4 * iters * chains * flops_per
+        res[name] = round(total / (best * 1e-3) / 1e12, 1)
+    return res
+
+
+def summarize_trace(path, warmup, steps):
+    """Per-kernel statistics of a rocprofv3 kernel trace (CSV) of one bench.py run, with the
+    warm-up dispatches (the first `warmup` of each step kernel) apart from the timed ones; prints
+    a markdown table."""
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    by = {}
+    for r in rows:
+        name = r.get("Kernel_Name") or r.get("KernelName") or r.get("Name")
+        t0 = int(r.get("Start_Timestamp") or r.get("BeginNs"))
+        t1 = int(r.get("End_Timestamp") or r.get("EndNs"))
+        by.setdefault(name, []).append((t0, (t1 - t0) / 1e3))
+    print("| Kernel | dispatches | warm-up avg (us) | timed dispatches | timed avg (us) | timed median (us) | timed min (us) | timed max (us) |")
+    print("|---|---|---|---|---|---|---|---|")
+    for name, v in sorted(by.items(), key=lambda kv: -sum(d for _, d in kv[1])):
+        v.sort()
+        d = [x for _, x in v]
+        if len(d) >= warmup + steps:
+            warm, timed = d[:warmup], d[warmup:warmup + steps]
+        else:
+            warm, timed = [], d
+        short = name if len(name) < 90 else name[:87] + "..."
+        wavg = f"{np.mean(warm):.1f}" if warm else "-"
+        print(f"| `{short}` | {len(d)} | {wavg} | {len(timed)} | {np.mean(timed):.1f} | "
+              f"{np.median(timed):.1f} | {np.min(timed):.1f} | {np.max(timed):.1f} |")
+
+
 def calibration_copy():
     """One plain device-to-device copy of CAL_BYTES (read CAL_BYTES, write CAL_BYTES), so that a
     rocprofv3 --pmc run of this script sees what FETCH_SIZE / WRITE_SIZE report for known bytes."""
@@ -565,6 +644,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-trace", default=None, metavar="KERNEL_TRACE_CSV",
+                    help="print per-kernel statistics of a rocprofv3 kernel trace of a bench.py run "
+                         "(warm-up dispatches apart from timed ones, by --warmup / --steps) and exit")
     ap.add_argument("--quantize-once", action="store_true",
                     help="quantize Q in a separate pass before the attention call (default: the "
                          "attention kernel quantizes Q itself, with bit-identical codes)")
@@ -573,6 +655,9 @@ def main():
                          "BK key tokens of a sequence (tilemix_quantize_blocks); a BK multiple of 64 "
                          "lets the attention kernel take one K scale per key tile")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.warmup, args.steps)
+        return
     args.scale_blocks = tuple(int(x) for x in args.scale_blocks.split(",")) if args.scale_blocks else None
     # Q stays fused (per token) when its blocks are single tokens
     args.fused_q = not args.quantize_once and (args.scale_blocks is None or args.scale_blocks[0] == 1)
@@ -611,29 +696,36 @@ def main():
     r = n8 / pairs
     flops = 4.0 * w.d * pairs
     # mixed floor: INT8 QK^T at the INT8 peak, FP16 QK^T and all P.V at the FP16 peak
-    t_floor = (2 * w.d * n8) / (PEAK_INT8 * 1e12) + (2 * w.d * (pairs - n8) + 2 * w.d * pairs) / (PEAK_FP16 * 1e12)
-    peak_mixed = flops / t_floor / 1e12
+    def mixed_peak(p_int8, p_fp16):
+        t_floor = (2 * w.d * n8) / (p_int8 * 1e12) + (2 * w.d * (pairs - n8) + 2 * w.d * pairs) / (p_fp16 * 1e12)
+        return flops / t_floor / 1e12
+    peak_mixed = mixed_peak(PEAK_INT8, PEAK_FP16)
 
     for _ in range(args.warmup):
         prob.step()
     torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for e0, e1, e2 in ev:
+    for e0, eq, e1, e2 in ev:
         e0.record(stream)
         prob.quantize()
+        eq.record(stream)
         prob.pack()
         e1.record(stream)
         prob.attention()
         e2.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    fwd_ms = float(np.mean([e1.elapsed_time(e2) for _, e1, e2 in ev]))
-    pre_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1, _ in ev]))
+    fwd = np.array([e1.elapsed_time(e2) for _, _, e1, e2 in ev])
+    steps_ev = np.array([e0.elapsed_time(e2) for e0, _, _, e2 in ev])
+    quant = np.array([e0.elapsed_time(eq) for e0, eq, _, _ in ev])
+    fwd_ms = float(np.mean(fwd))
+    pre_ms = float(np.mean([e0.elapsed_time(e1) for e0, _, e1, _ in ev]))
+    quant_ms = float(np.median(quant))
     step_ms = wall * 1e3 / args.steps
+    peaks = measure_mfma_peaks(stream)
 
     tflops = flops / (step_ms * 1e-3) / 1e12
     fwd_tflops = flops / (fwd_ms * 1e-3) / 1e12
@@ -641,7 +733,7 @@ def main():
     q_bytes = w.total * ((0 if args.fused_q else w.hq) + (0 if w.kv_int8 else w.hk)) * (w.d * 3 + 4)
 
     result = {
-        "metric": "causal prefill attention TFLOPS & % MFMA roofline at L=32k, d=128, GQA",
+        "metric": prefill_metric(w),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -664,17 +756,30 @@ def main():
         },
         "pct_mixed_roofline": round(100 * tflops / peak_mixed, 2),
         "pct_fp16_roofline": round(100 * tflops / PEAK_FP16, 2),
+        "ms_per_step_events": {"mean": round(float(np.mean(steps_ev)), 4),
+                               "median": round(float(np.median(steps_ev)), 4),
+                               "min": round(float(np.min(steps_ev)), 4)},
         "fwd_ms": round(fwd_ms, 4),
+        "fwd_ms_median": round(float(np.median(fwd)), 4),
+        "fwd_ms_min": round(float(np.min(fwd)), 4),
         "quantize_pack_ms": round(pre_ms, 4),
-        "quantize_gbps": round(q_bytes / (pre_ms * 1e-3) / 1e9, 1) if q_bytes else None,
+        "quantize_ms_median": round(quant_ms, 4),
+        "quantize_gbps": round(q_bytes / (quant_ms * 1e-3) / 1e9, 1) if q_bytes else None,
         "roofline": {
-            "kernel": f"prefill_fwd_kernel<{w.d}, {str(bool(w.kv_int8)).lower()}, false, "
-                      f"{str(prob.k_scale_block > 0).lower()}> (+ vt_pack pre-pass in the timed call)",
+            # instance 0 is the production kernel (per-key K scales), 2 the block-scale one
+            "kernel": f"prefill_fwd_kernel<{w.d}, {str(bool(w.kv_int8)).lower()}, "
+                      f"{2 if prob.k_scale_block > 0 else 0}> (+ vt_pack pre-pass in the timed call)",
             "bound": "mfma",
             "achieved": round(fwd_tflops, 2),
             "peak": round(peak_mixed, 1),
             "unit": "TFLOP/s",
             "frac": round(fwd_tflops / peak_mixed, 4),
+            "peak_measured": round(mixed_peak(peaks["int8"], peaks["fp16"]), 1),
+            "frac_measured": round(fwd_tflops / mixed_peak(peaks["int8"], peaks["fp16"]), 4),
+            "mfma_peaks": {"int8_spec": PEAK_INT8, "int8_measured": peaks["int8"],
+                           "fp16_spec": PEAK_FP16, "fp16_measured": peaks["fp16"],
+                           "how": "libtilemix_peak.so: 16384 wavefronts issuing 4 independent "
+                                  "32x32 MFMA chains, best of 5 launches"},
             # the committed counters were taken on this workload's default configuration only
             "traffic": measured_traffic() if (args.workload == WORKLOAD and args.fused_q) else None,
             "flops_per_launch": flops,

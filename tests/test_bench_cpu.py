@@ -60,3 +60,30 @@ def test_pages_context_is_marked_as_context():
     assert c["hardware"].startswith("NVIDIA A100")
     assert c["flashattention_fp16"] == 14.33 and c["tilemix_75pct_groups_int8"] == 31.80
     assert "not comparable" in c["note"]
+
+
+def test_prefill_metric_strings():
+    """The headline workload carries the headline metric; the others name their own shape."""
+    assert bench.prefill_metric(wl.make("gqa32k")) == \
+        "causal prefill attention TFLOPS & % MFMA roofline at L=32k, d=128, GQA"
+    assert bench.prefill_metric(wl.make("mha8k")).endswith("at L=8k, d=128, MHA")
+    assert "INT8 K/V cache" in bench.prefill_metric(wl.make("kvint8_128k"))
+    assert "varlen batch of 8 sequences" in bench.prefill_metric(wl.make("varlen64k"))
+    assert bench.prefill_metric(wl.make("tiny")).endswith("at L=256, d=64, MHA")
+
+
+def test_summarize_trace_splits_warmup(tmp_path, capsys):
+    """Warm-up dispatches (the first `warmup` of each kernel) are reported apart from the timed ones."""
+    path = tmp_path / "kernel_trace.csv"
+    lines = ["Kernel_Name,Start_Timestamp,End_Timestamp"]
+    t = 0
+    for i in range(5):  # 2 warm-up + 3 timed dispatches of one kernel: 9 us, then 4 us each
+        d = 9000 if i < 2 else 4000
+        lines.append(f"k<1>,{t},{t + d}")
+        t += 10000
+    path.write_text("\n".join(lines) + "\n")
+    bench.summarize_trace(str(path), warmup=2, steps=3)
+    out = capsys.readouterr().out
+    row = [r for r in out.splitlines() if r.startswith("| `k<1>`")][0]
+    cells = [c.strip() for c in row.split("|")[1:-1]]
+    assert cells[1] == "5" and cells[2] == "9.0" and cells[3] == "3" and cells[4] == "4.0"

@@ -358,6 +358,51 @@ def test_full_size_sampled_parity(name):
           f"(fused Q, fp16 out), INT8 pairs {n8 / nall:.3f}")
 
 
+def test_mha8k_full_output_parity():
+    """Every row and head of the 8k MHA workload against the oracle (about 1.1e9 legal query-key
+    pairs on the host), in both launch configurations."""
+    w = named("mha8k")
+    ref, ref_lse, n8, nall = oracle.prepare(w).prefill()
+    prob = run(w)
+    err = check_out(prob.out.cpu().numpy(), ref, "mha8k (all rows)")
+    check_lse(prob.lse.cpu().numpy(), ref_lse, "mha8k (all rows)")
+    del prob
+    bench_cfg = DeviceProblem(w, out_dtype=torch.float16, fused_q=True)
+    bench_cfg.step()
+    torch.cuda.synchronize()
+    err16 = check_out(bench_cfg.out.float().cpu().numpy(), ref, "mha8k (all rows, fused Q, fp16 out)",
+                      fp16_out=True)
+    check_lse(bench_cfg.lse.cpu().numpy(), ref_lse, "mha8k (all rows, fused Q, fp16 out)")
+    print(f"mha8k: all {w.total} rows x {w.hq} heads, max err {err:.2e} (fp32 out), {err16:.2e} "
+          f"(fused Q, fp16 out), INT8 pairs {n8 / nall:.3f}")
+
+
+def route_row_edges(w):
+    """The first and the last query row of every route row of every sequence."""
+    rows = set()
+    for b, L in enumerate(w.seqlens):
+        base = int(w.cu_seqlens[b])
+        for m0 in range(0, L, w.bm_r):
+            rows.add(base + m0)
+            rows.add(base + min(m0 + w.bm_r, L) - 1)
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def test_varlen64k_route_row_edges_parity():
+    """The first and last query row of every route row of every sequence of the varlen batch (all
+    heads), in the configuration bench.py times."""
+    w = named("varlen64k")
+    rows = route_row_edges(w)
+    ref, ref_lse, _, _ = oracle.prepare(w).prefill(rows)
+    idx = torch.from_numpy(rows).cuda()
+    prob = DeviceProblem(w, out_dtype=torch.float16, fused_q=True)
+    prob.step()
+    torch.cuda.synchronize()
+    err = check_out(prob.out[idx].float().cpu().numpy(), ref, "varlen64k route-row edges", fp16_out=True)
+    check_lse(prob.lse[:, idx].cpu().numpy(), ref_lse, "varlen64k route-row edges")
+    print(f"varlen64k: {len(rows)} route-row edge rows x {w.hq} heads, max err {err:.2e}")
+
+
 @pytest.mark.parametrize("name", ["gqa32k", "kvint8_128k"])
 def test_full_size_int32_dump(name):
     """Dumped int32 accumulators of the first, middle and last query tiles, with Q quantized by the
