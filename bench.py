@@ -602,6 +602,10 @@ def run_numerics(args):
             prob.step()
             torch.cuda.synchronize()
             out = prob.out.cpu().numpy().astype(np.float64)
+            # the same inputs and routes with the online-softmax state kept in binary16
+            prob.attention(state_fp16=True)
+            torch.cuda.synchronize()
+            out_s16 = prob.out.cpu().numpy().astype(np.float64)
             n8 = int8_pair_counts(w)
             del prob
             # the same point with per-block scales: one per 64-token block of Q and of K
@@ -614,6 +618,8 @@ def run_numerics(args):
                 "mean_abs_dev": float(np.abs(out - exact).mean()),
                 "max_abs_dev": float(np.abs(out - exact).max()),
                 "mean_abs_dev_block_scales": float(np.abs(out_b - exact).mean()),
+                "mean_abs_dev_fp16_state": float(np.abs(out_s16 - exact).mean()),
+                "max_abs_dev_fp16_state": float(np.abs(out_s16 - exact).max()),
                 "int8_pair_fraction": round(n8 / (w.legal_pairs() * w.hq), 4),
             }
         table[str(L)] = row
@@ -630,7 +636,9 @@ def run_numerics(args):
                    "route_tile": [64, 64], "group": 1, "lengths": list(workloads.NUMERICS_LENGTHS),
                    "int8_coverages": list(workloads.NUMERICS_COVERAGES),
                    "reference": "exact causal attention of the fp16 inputs, fp64, PyTorch CPU",
-                   "scales": "per token (mean_abs_dev) and per 64-token block (mean_abs_dev_block_scales)"},
+                   "scales": "per token (mean_abs_dev) and per 64-token block (mean_abs_dev_block_scales)",
+                   "state": "fp32 online-softmax state, and binary16 state rounded after every 64-key "
+                            "tile (*_fp16_state, per-token scales)"},
         "table": table,
         "seconds": round(time.perf_counter() - t0, 1),
     }
