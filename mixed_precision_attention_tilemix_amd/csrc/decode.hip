@@ -100,8 +100,9 @@ __device__ __forceinline__ float wave_max(float v) { return wave_reduce<true>(v)
 // key 16 (t >> 3) + 8 hl + (t & 7) of the tile, the layout the P.V MFMA takes P in.
 __device__ __forceinline__ int perm32(int r) { return (r & 0x13) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-// Eight signed bytes to fp16, exactly: each byte + 128 becomes the low byte of the fp16 number
-// 1024 + (byte + 128) (high byte 0x64, by a byte permute), and 1152 is subtracted.
+// Eight signed bytes to fp16, exactly, by the magic-number (exponent-bias) conversion: each
+// byte + 128 becomes the low byte of the fp16 number 1024 + (byte + 128) (high byte 0x64, whose
+// mantissa unit is 1, by a byte permute), and 1152 is subtracted.
 __device__ __forceinline__ half8v i8x8_to_f16(int2v v) {
   half8v r;
 #pragma unroll
