@@ -789,7 +789,8 @@ def main():
                            "how": "libtilemix_peak.so: 16384 wavefronts issuing 4 independent "
                                   "32x32 MFMA chains, best of 5 launches"},
             # the committed counters were taken on this workload's default configuration only
-            "traffic": measured_traffic() if (args.workload == WORKLOAD and args.fused_q) else None,
+            "traffic": measured_traffic() if (args.workload == WORKLOAD and args.fused_q
+                                              and args.scale_blocks is None) else None,
             "flops_per_launch": flops,
             "peak_note": f"mixed MFMA peak for INT8 fraction {r:.4f}: INT8 QK^T at {PEAK_INT8}, "
                          f"FP16 QK^T and P.V at {PEAK_FP16} TFLOP/s",
