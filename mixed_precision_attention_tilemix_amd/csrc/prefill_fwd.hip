@@ -31,7 +31,9 @@
 //   measured slower: its extra live registers pushed the kernel into spills. One barrier per
 //   64-key tile; the next tile's K (fp16 and/or int8, as the route bits of the workgroup ask),
 //   V^T and per-key factors are fetched with direct global->LDS loads while the current tile is
-//   computed.
+//   computed. The queries never pass through LDS: each lane keeps its row's fp16 fragments (the
+//   FP16 route's B operand, 32 registers at head_dim 128) and int8 fragments in registers, which
+//   leaves LDS to the K / V^T / factor stages (80.5 KiB at head_dim 128).
 //
 // Softmax
 //   Base 2, with the score scale folded into one FMA per element. The running max is only
@@ -66,12 +68,11 @@ constexpr float P_LIMIT = 32768.0f;  // fast path: a lane's sum of P over a tile
 // distinct banks.
 template <int D>
 struct Smem {
-  static constexpr int RB16 = D * 2;  // bytes per fp16 row of K / Q
+  static constexpr int RB16 = D * 2;  // bytes per fp16 row of K
   static constexpr int RB8 = D;       // bytes per int8 row of K8
   static constexpr int C16 = RB16 / 16;
   static constexpr int C8 = RB8 / 16;
-  static constexpr int Q16 = 0;                   // [BM][D] fp16 Q of the workgroup
-  static constexpr int KBUF = Q16 + BM * RB16;    // two K stages
+  static constexpr int KBUF = 0;                  // two K stages
   static constexpr int K16 = 0;                   // offsets inside one K stage
   static constexpr int K8 = K16 + BN * RB16;
   static constexpr int KSTAGE = K8 + BN * RB8;
@@ -259,9 +260,10 @@ struct Wave {
   // LDS byte offsets of this lane's operand rows: chunk (2*i + hl) ^ f of a row whose length is a
   // multiple of 128 bytes sits at row_start + 16*(hl ^ f) XOR 32*i, since 2*i + hl = 2*i ^ hl
   int kbase8, vbase;      // K8 row (i = ks), V^T row (i = 16-key step)
-  int kbase16, qbase16;   // fp16 K and Q rows (i = ks)
+  int kbase16;            // fp16 K row (i = ks)
   int fkey;               // key (within a 32-key half) whose factor this lane loads for its row
   int4v q8f[D / 32];
+  half8v q16f[D / 16];  // fp16 Q fragments of this lane's query row: channels 16 ks + 8 hl + 0..7
   float cq;        // q_scale * softmax_scale * log2(e), floored so that 0 * -inf cannot occur
   float cs;        // softmax_scale * log2(e)
   float16v o[D / 32];  // O^T accumulator
@@ -295,12 +297,12 @@ struct Wave {
   }
 
   // FP16: the two chains interleaved, one Q fragment feeding both.
-  __device__ __forceinline__ void qk_f16(const char* kst, const char* q16) {
+  __device__ __forceinline__ void qk_f16(const char* kst) {
     using L = Smem<D>;
     float16v a0 = {}, a1 = {};
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      const half8v qv = *reinterpret_cast<const half8v*>(q16 + (qbase16 ^ (32 * ks)));
+      const half8v qv = q16f[ks];
       const half8v k0 = *reinterpret_cast<const half8v*>(kst + L::K16 + (kbase16 ^ (32 * ks)));
       const half8v k1 = *reinterpret_cast<const half8v*>(kst + L::K16 + 32 * L::RB16 + (kbase16 ^ (32 * ks)));
       a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0, qv, a0, 0, 0, 0);
@@ -464,26 +466,19 @@ struct DumpCtx {
 };
 
 // Fused Q quantization (the alternative to the quantize-once pass): the two lanes of a query row
-// (hl = 0, 1) each read, from the workgroup's fp16 Q in LDS, the channels [32 ks + 16 hl, +16)
-// they feed to the INT8 MFMA, share the row's absolute maximum, and compute the same codes and
-// scale as the quantize-once pass (same fp32 operations: a = max|x|, inv = 127 / a and a / 127
-// correctly rounded, rint, clamp). Returns the scale.
+// (hl = 0, 1) hold its fp16 channels 16 k + 8 hl + 0..7 (k = 0 .. D/16-1); they share the row's
+// absolute maximum and compute the same codes and scale as the quantize-once pass (same fp32
+// operations: a = max|x|, inv = 127 / a and a / 127 correctly rounded, rint, clamp). The INT8
+// score MFMA wants lane hl to hold channels 32 ks + 16 hl + 0..15, so each lane then swaps one
+// 8-code group per 32 channels with its partner lane (lane ^ 32). Returns the scale. Every lane
+// of the wavefront must call it (the exchanges are wave-wide).
 template <int D>
-__device__ __forceinline__ float quantize_q_half(const char* q16, int row, int hl, int4v (&q8f)[D / 32]) {
-  using L = Smem<D>;
-  const char* base = q16 + row * L::RB16;
-  const int f = L::f16(row);
-  half8v xv[D / 16];
-#pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks) {
-    xv[2 * ks] = *reinterpret_cast<const half8v*>(base + 16 * ((4 * ks + 2 * hl) ^ f));
-    xv[2 * ks + 1] = *reinterpret_cast<const half8v*>(base + 16 * ((4 * ks + 2 * hl + 1) ^ f));
-  }
+__device__ __forceinline__ float quantize_q_regs(const half8v (&q16f)[D / 16], int hl, int4v (&q8f)[D / 32]) {
   float am = 0.0f;
 #pragma unroll
-  for (int i = 0; i < D / 16; ++i)
+  for (int k = 0; k < D / 16; ++k)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(static_cast<float>(xv[i][e])));
+    for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(static_cast<float>(q16f[k][e])));
   am = fmaxf(am, __shfl_xor(am, 32));  // the row's other half
   float s = 0.0f;
   float inv = 0.0f;
@@ -491,16 +486,29 @@ __device__ __forceinline__ float quantize_q_half(const char* q16, int row, int h
     inv = 127.0f / am;
     s = am / 127.0f;
   }
+  int2v codes[D / 16];  // 8 codes of each fp16 fragment
+#pragma unroll
+  for (int k = 0; k < D / 16; ++k) {
+    int2v packed = {};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float c = rintf(static_cast<float>(q16f[k][e]) * inv);
+      c = fminf(fmaxf(c, -127.0f), 127.0f);
+      packed[e / 4] |= static_cast<int>(static_cast<uint32_t>(static_cast<uint8_t>(static_cast<int8_t>(c))) << (8 * (e % 4)));
+    }
+    codes[k] = packed;
+  }
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks) {
-    int4v packed = {};
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float c = rintf(static_cast<float>(xv[2 * ks + i / 8][i % 8]) * inv);
-      c = fminf(fmaxf(c, -127.0f), 127.0f);
-      packed[i / 4] |= static_cast<int>(static_cast<uint32_t>(static_cast<uint8_t>(static_cast<int8_t>(c))) << (8 * (i % 4)));
-    }
-    q8f[ks] = packed;
+    // lane hl = 0 keeps channels 32 ks + 0..7 and needs 32 ks + 8..15 (the partner's fragment
+    // 2 ks); lane hl = 1 keeps 32 ks + 24..31 and needs 32 ks + 16..23 (the partner's 2 ks + 1)
+    const int2v send = hl ? codes[2 * ks] : codes[2 * ks + 1];
+    int2v recv;
+    recv[0] = __shfl_xor(send[0], 32);
+    recv[1] = __shfl_xor(send[1], 32);
+    const int2v lo = hl ? recv : codes[2 * ks];
+    const int2v hi = hl ? codes[2 * ks + 1] : recv;
+    q8f[ks] = int4v{lo[0], lo[1], hi[0], hi[1]};
   }
   return s;
 }
@@ -573,7 +581,6 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
   char* const kbuf = smem + L::KBUF;
   char* const vbuf = smem + L::VBUF;
   char* const sbuf = smem + L::SBUF;
-  const char* const q16w = smem + L::Q16;
 
   Wave<D, KV8, KBLK> wv;
   wv.hl = hl;
@@ -583,20 +590,20 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
   {
     const int kr = perm32(r32);  // K row this lane feeds to the MFMA
     wv.kbase16 = kr * L::RB16 + 16 * (hl ^ L::f16(kr));
-    wv.qbase16 = (ROWS_W * w + r32) * L::RB16 + 16 * (hl ^ L::f16(ROWS_W * w + r32));
     wv.kbase8 = kr * L::RB8 + 16 * (hl ^ L::f8(kr));
     wv.vbase = r32 * (BN * 2) + 16 * (hl ^ vt_swizzle(r32));
     wv.fkey = 16 * ((lane & 15) >> 3) + 8 * hl + (lane & 7);
   }
 
-  // ---- resident queries: fp16 Q of the workgroup in LDS, this wave's int8 Q in registers
-  for (int ch = tid; ch < BM * L::C16; ch += NW * 64) {
-    const int row = ch / L::C16, col = ch % L::C16;
-    int4v val = {};
-    if (q0 + row < Lq)
-      val = *reinterpret_cast<const int4v*>(a.q + (q_begin + q0 + row) * a.q_stride_tok +
-                                            static_cast<int64_t>(h) * a.q_stride_head + col * 8);
-    *reinterpret_cast<int4v*>(smem + L::Q16 + row * L::RB16 + 16 * (col ^ L::f16(row))) = val;
+  // ---- resident queries, in registers: each lane's fp16 Q fragments (the B operand of the FP16
+  // score MFMAs) straight from global memory, and its int8 Q fragments
+  if (wv.row_valid) {
+    const _Float16* qrow = a.q + (q_begin + wv.my_q) * a.q_stride_tok + static_cast<int64_t>(h) * a.q_stride_head;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) wv.q16f[ks] = *reinterpret_cast<const half8v*>(qrow + 16 * ks + 8 * hl);
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) wv.q16f[ks] = half8v{};
   }
   wv.cq = 1e-30f;
   wv.cs = a.scale_log2;
@@ -638,9 +645,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
 
   // fused Q quantization: each lane quantizes its half of its query row from the fp16 tile in LDS
   if (a.q8 == nullptr) {
-    __syncthreads();  // publishes the fp16 Q stores
-    if (wv.row_valid)
-      wv.cq = fmaxf(quantize_q_half<D>(q16w, ROWS_W * w + r32, hl, wv.q8f) * a.scale_log2, 1e-30f);
+    const float qs = quantize_q_regs<D>(wv.q16f, hl, wv.q8f);  // every lane: exchanges with lane ^ 32
+    if (wv.row_valid) wv.cq = fmaxf(qs * a.scale_log2, 1e-30f);
   }
 
   // ---- prologue: K, V^T and factors of tile 0 (the single-buffered instance loads every tile in
@@ -676,7 +682,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
         wv.qk_i8(kst);
         if constexpr (DUMP) wv.dump_i8(j0 <= dc.act_limit ? dc.row : nullptr, j0, dc.Lk, dc.bn_r, dc.tile_stride);
       } else {
-        wv.qk_f16(kst, q16w);
+        wv.qk_f16(kst);
       }
       const float f0 = wv.template load_f<0>(scl);
       const float f1 = wv.template load_f<1>(scl);
