@@ -39,9 +39,11 @@
 //   Base 2, with the score scale folded into one FMA per element. The running max is only
 //   raised when needed: each tile is exponentiated against the current max, and only if some
 //   lane's sum of P over the tile exceeds 2^15 (so that no P can overflow fp16) or the row has
-//   no max yet does the wavefront take the slow path, which takes the true max, rescales O and
-//   l and recomputes P. The row sum is taken from the fp16-rounded P that also feeds P.V and is kept
-//   per lane half until the epilogue.
+//   no max yet (the wavefront's first tile) does the wavefront take the slow path, which takes
+//   the true max, rescales O and l and recomputes P. The row sum is taken from the fp16-rounded
+//   P that also feeds P.V (one running sum over both key halves of a tile) and is kept per lane
+//   half until the epilogue. P is assembled from packed fp16 pairs (32-bit words), so that the
+//   slow path's join merges whole registers instead of re-packing halves.
 //
 // INT8 scores
 //   The int32 accumulator is converted to fp32 and multiplied by the key's k_scale (gathered per
@@ -271,6 +273,7 @@ struct Wave {
   float c[2];          // per-row factor of each half to log2 units: cq (INT8) or cs (FP16)
   half8v p[2][2];      // fp16 P of the two key halves, [half][16-key step]
   float m, m_use, l;   // running max (log2 units), its finite stand-in, this lane's row sum
+  bool have_max;       // wave-uniform: the first tile's slow path has run
 
   // s[0], s[1] = raw scores of the two key halves of the K tile in stage kst: int32
   // accumulators (as bits) for INT8, fp32 dot products for FP16; convert_f turns them into
@@ -391,24 +394,23 @@ struct Wave {
       if (key0 + 16 * (t >> 3) + 8 * hl + (t & 7) > lim) s[KB][t] = -INFINITY;
   }
 
-  // p[KB] = fp16 exp2(s * c - m_use) of half KB; returns this lane's sum of the rounded P.
+  // p[KB] = fp16 exp2(s * c - m_use) of half KB; returns rs plus this lane's sum of the rounded
+  // P (the second half continues the first half's sum).
   template <int KB>
-  __device__ __forceinline__ float softmax() {
-    float rs = 0.0f;
+  __device__ __forceinline__ float softmax(float rs) {
     const float ck = c[KB];
 #pragma unroll
     for (int g8 = 0; g8 < 2; ++g8) {
-      half8v pb;
+      int4v pw;  // built from packed pairs, so that the slow path's join merges whole dwords
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         const float x0 = __builtin_fmaf(s[KB][8 * g8 + e], ck, -m_use);
         const float x1 = __builtin_fmaf(s[KB][8 * g8 + e + 1], ck, -m_use);
         const half2v h2 = pk(fast_exp2(x0), fast_exp2(x1));
-        pb[e] = h2[0];
-        pb[e + 1] = h2[1];
+        pw[e / 2] = __builtin_bit_cast(int, h2);
         rs = __builtin_amdgcn_fdot2(h2, half2v{static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)}, rs, false);
       }
-      p[KB][g8] = pb;
+      p[KB][g8] = __builtin_bit_cast(half8v, pw);
     }
     return rs;
   }
@@ -418,7 +420,7 @@ struct Wave {
   // EXACT (the FP16-state instance): the max is raised whenever a score exceeds it, as in the
   // plain online recurrence, so that P <= 1 and the row sum stays within binary16 range.
   template <bool EXACT>
-  __device__ __forceinline__ void settle_tile(float rs0, float rs1) {
+  __device__ __forceinline__ void settle_tile(float rs) {
     float mx = -INFINITY;
     if constexpr (EXACT) {
 #pragma unroll
@@ -426,7 +428,10 @@ struct Wave {
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       mx = static_cast<float>(static_cast<_Float16>(mx));  // the max is state: binary16
     }
-    if (__any(row_valid && (EXACT ? mx > m : (!(rs0 + rs1 <= P_LIMIT) || m == -INFINITY)))) {
+    // (lazy form: the first tile always takes the slow path, which gives every row with a legal
+    // key its max; a row without one keeps m = -inf and P = 0)
+    if ((EXACT || have_max) ? __any(row_valid && (EXACT ? mx > m : !(rs <= P_LIMIT))) : true) {
+      have_max = true;
       if constexpr (!EXACT) {
 #pragma unroll
         for (int t = 0; t < 16; ++t) mx = fmaxf(mx, fmaxf(s[0][t] * c[0], s[1][t] * c[1]));
@@ -440,10 +445,9 @@ struct Wave {
         m = mx;
         m_use = mx;
       }
-      rs0 = softmax<0>();
-      rs1 = softmax<1>();
+      rs = softmax<1>(softmax<0>(0.0f));
     }
-    l += rs0 + rs1;
+    l += rs;
   }
 
   // The state kept between tiles rounded to binary16 (round to nearest even) and widened back:
@@ -620,6 +624,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) wv.o[i] = float16v{};
   wv.m = -INFINITY;
+  wv.have_max = false;
   wv.m_use = 0.0f;
   wv.l = 0.0f;
 
@@ -699,9 +704,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
         wv.template mask<0>(j0);
         wv.template mask<1>(j0 + 32);
       }
-      const float rs0 = wv.template softmax<0>();
-      const float rs1 = wv.template softmax<1>();
-      wv.template settle_tile<F16S>(rs0, rs1);
+      wv.template settle_tile<F16S>(wv.template softmax<1>(wv.template softmax<0>(0.0f)));
       half8v vf1[2][D / 32];
       wv.template load_v<1>(vst, vf1);
       wv.template pv_regs<0>(vf0);
