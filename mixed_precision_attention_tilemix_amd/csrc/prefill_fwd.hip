@@ -21,19 +21,19 @@
 // Schedule (per wavefront, one 64-key tile per iteration)
 //   After the tile's barrier each wavefront reads all K fragments of the tile and issues the
 //   score MFMAs of both 32-key halves (two interleaved accumulator chains), reads the per-key
-//   factors and the first half's V^T fragments, converts and exponentiates both halves (VALU)
-//   with one slow-path check for the tile, then reads the second half's V^T fragments and
-//   issues both halves' P.V MFMAs; the other wavefront of the SIMD fills the gaps. Operand reads
+//   factors, converts and exponentiates both halves (VALU) with one slow-path check for the
+//   tile, then reads the V^T fragments and issues both halves' P.V MFMAs. The two wavefronts
+//   that share a SIMD (w and w + 4) take these steps in different orders: the second one runs
+//   the P.V of the previous tile before the scores of the current one, so that one tends to
+//   issue MFMAs while the other runs its softmax (V^T keeps three stages for it). Operand reads
 //   are issued ahead of their MFMAs so that each waits only for its own data: the direct loads
 //   are written as inline assembly, because the compiler counts a pending direct load against
-//   the LDS counter too and would then wait for every LDS read to finish before each MFMA. A
-//   deeper software pipeline across tiles (scores of the next tile during this tile's softmax)
-//   measured slower: its extra live registers pushed the kernel into spills. One barrier per
-//   64-key tile; the next tile's K (fp16 and/or int8, as the route bits of the workgroup ask),
-//   V^T and per-key factors are fetched with direct global->LDS loads while the current tile is
-//   computed. The queries never pass through LDS: each lane keeps its row's fp16 fragments (the
-//   FP16 route's B operand, 32 registers at head_dim 128) and int8 fragments in registers, which
-//   leaves LDS to the K / V^T / factor stages (80.5 KiB at head_dim 128).
+//   the LDS counter too and would then wait for every LDS read to finish before each MFMA. One
+//   barrier per 64-key tile; the next tile's K (fp16 and/or int8, as the route bits of the
+//   workgroup ask), V^T and per-key factors are fetched with direct global->LDS loads while the
+//   current tile is computed. The queries never pass through LDS: each lane keeps its row's fp16
+//   fragments (the FP16 route's B operand, 32 registers at head_dim 128) and int8 fragments in
+//   registers, which leaves LDS to the K / V^T / factor stages (96.5 KiB at head_dim 128).
 //
 // Softmax
 //   Base 2, with the score scale folded into one FMA per element. The running max is only
@@ -78,9 +78,9 @@ struct Smem {
   static constexpr int K16 = 0;                   // offsets inside one K stage
   static constexpr int K8 = K16 + BN * RB16;
   static constexpr int KSTAGE = K8 + BN * RB8;
-  static constexpr int VBUF = KBUF + 2 * KSTAGE;  // two V^T stages, [D][BN] fp16 as vt_pack.hip
+  static constexpr int VBUF = KBUF + 2 * KSTAGE;  // three V^T stages, [D][BN] fp16 as vt_pack.hip
   static constexpr int VSTAGE = D * BN * 2;
-  static constexpr int SBUF = VBUF + 2 * VSTAGE;  // two slots of per-key factors
+  static constexpr int SBUF = VBUF + 3 * VSTAGE;  // two slots of per-key factors
   static constexpr int SSLOT = BN * 4;            // k_scale of the tile's keys
   static constexpr int BYTES = SBUF + 2 * SSLOT;
   // The 16 lanes served together read 16 different rows at one chunk index: XOR-ing the chunk
@@ -662,18 +662,34 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
     stg.s_next(sbuf);
   }
 
-  // ---- main loop: iteration n computes tile n (scores of both halves, their softmax, P.V) while
-  // the direct loads of tile n+1 fly
+  // ---- main loop. Iteration n: the direct loads of tile n+1 fly while tile n is computed. The
+  // two wavefronts that share a SIMD (w and w + NW/2) take the tile's steps in different orders:
+  // wave w < NW/2 does scores, softmax and P.V of tile n; wave w >= NW/2 does the P.V of tile
+  // n-1 first, then the scores and softmax of tile n (its P.V follows in iteration n+1), so that
+  // one issues matrix-core work while the other runs its softmax. V^T therefore keeps three
+  // stages (tiles n-1, n, n+1); K and the factors keep two.
+  const bool lag = w >= NW / 2;  // wave-uniform
+  int vs_prev = 2, vs_cur = 0, vs_next = 1;  // V^T stages of tiles n-1, n, n+1
+  auto pv_tile = [&](const char* vst) {
+    half8v va[2][D / 32], vb[2][D / 32];
+    wv.template load_v<0>(vst, va);
+    wv.template load_v<1>(vst, vb);
+    wv.template pv_regs<0>(va);
+    wv.template pv_regs<1>(vb);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 * (D / 32), 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * (D / 32), 0);
+    if constexpr (F16S) wv.round_state_fp16();
+  };
   for (int n = 0; n < n_tiles; ++n) {
-    dma_barrier();  // tile n landed; the stages of tile n-1 are free
+    dma_barrier();  // tile n landed; the K / factor stages of tile n-1 and the V^T stage of n-2 are free
     if constexpr (SYNC) {
       stg.k_next(kbuf, rb0 != full, rb0 != 0u);
-      stg.v_next(vbuf);
+      stg.v_next(vbuf + vs_cur * L::VSTAGE);
       stg.s_next(sbuf);
       dma_barrier();
     } else if (n + 1 < n_tiles) {
       stg.k_next(kbuf + ((n + 1) & 1) * L::KSTAGE, rb1 != full, rb1 != 0u);
-      stg.v_next(vbuf + ((n + 1) & 1) * L::VSTAGE);
+      stg.v_next(vbuf + vs_next * L::VSTAGE);
       stg.s_next(sbuf + ((n + 1) & 1) * L::SSLOT);
     }
     if (wave_live) {
@@ -681,8 +697,9 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
       const bool i8 = (rb0 >> my_rl) & 1u;
       const int st = SYNC ? 0 : (n & 1);
       const char* kst = kbuf + st * L::KSTAGE;
-      const char* vst = vbuf + st * L::VSTAGE;
+      const char* vst = vbuf + vs_cur * L::VSTAGE;
       const float* scl = reinterpret_cast<const float*>(sbuf + st * L::SSLOT);
+      if (lag && n > 0) pv_tile(vbuf + vs_prev * L::VSTAGE);
       if (i8) {
         wv.qk_i8(kst);
         if constexpr (DUMP) wv.dump_i8(j0 <= dc.act_limit ? dc.row : nullptr, j0, dc.Lk, dc.bn_r, dc.tile_stride);
@@ -691,8 +708,6 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
       }
       const float f0 = wv.template load_f<0>(scl);
       const float f1 = wv.template load_f<1>(scl);
-      half8v vf0[2][D / 32];
-      wv.template load_v<0>(vst, vf0);
       if (i8) {
         wv.template convert_f<0, true>(f0);
         wv.template convert_f<1, true>(f1);
@@ -705,15 +720,12 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
         wv.template mask<1>(j0 + 32);
       }
       wv.template settle_tile<F16S>(wv.template softmax<1>(wv.template softmax<0>(0.0f)));
-      half8v vf1[2][D / 32];
-      wv.template load_v<1>(vst, vf1);
-      wv.template pv_regs<0>(vf0);
-      wv.template pv_regs<1>(vf1);
-      // the second half's V^T reads first, then all P.V MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 32), 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 4 * (D / 32), 0);
-      if constexpr (F16S) wv.round_state_fp16();
+      if (!lag) pv_tile(vst);
     }
+    const int vs_free = vs_prev;
+    vs_prev = vs_cur;
+    vs_cur = vs_next;
+    vs_next = vs_free;
     rb0 = rb1;
     // tile n+2's position in its routing group, kept as a counter (no division per tile)
     if (pos2 == 0 && n + 2 < n_tiles) rb1 = group_bits(wrow, a.wpr, nrr, grp2);
@@ -722,6 +734,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
       ++grp2;
     }
   }
+  if (lag && wave_live && n_tiles > 0) pv_tile(vbuf + vs_prev * L::VSTAGE);  // P.V of the last tile
 
   // ---- epilogue: O = O^T / l, LSE = (m + log2 l) * ln 2
   const float l_row = wv.l + __shfl_xor(wv.l, 32);
