@@ -259,6 +259,7 @@ struct Wave {
   int hl, my_q;
   int lim;         // last legal key (sequence-local) of this lane's query
   bool row_valid;
+  uint64_t valid_lanes;  // wave-uniform ballot of row_valid
   // LDS byte offsets of this lane's operand rows: chunk (2*i + hl) ^ f of a row whose length is a
   // multiple of 128 bytes sits at row_start + 16*(hl ^ f) XOR 32*i, since 2*i + hl = 2*i ^ hl
   int kbase8, vbase;      // K8 row (i = ks), V^T row (i = 16-key step)
@@ -430,7 +431,9 @@ struct Wave {
     }
     // (lazy form: the first tile always takes the slow path, which gives every row with a legal
     // key its max; a row without one keeps m = -inf and P = 0)
-    if ((EXACT || have_max) ? __any(row_valid && (EXACT ? mx > m : !(rs <= P_LIMIT))) : true) {
+    if ((EXACT || have_max)
+            ? (__builtin_amdgcn_ballot_w64(EXACT ? mx > m : !(rs <= P_LIMIT)) & valid_lanes) != 0
+            : true) {
       have_max = true;
       if constexpr (!EXACT) {
 #pragma unroll
@@ -591,6 +594,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
   wv.my_q = qa + r32;
   wv.lim = a.causal ? min(Lk - 1, wv.my_q + off) : Lk - 1;
   wv.row_valid = wv.my_q < Lq;
+  wv.valid_lanes = __builtin_amdgcn_ballot_w64(wv.row_valid);
   {
     const int kr = perm32(r32);  // K row this lane feeds to the MFMA
     wv.kbase16 = kr * L::RB16 + 16 * (hl ^ L::f16(kr));
