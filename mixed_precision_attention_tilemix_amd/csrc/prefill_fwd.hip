@@ -242,7 +242,8 @@ typedef const __attribute__((address_space(4))) int32_t const_i32;
 __device__ __forceinline__ int ld_uniform(const int32_t* p, int i) { return ((const const_i32*)p)[i]; }
 
 // Route bits of the workgroup's route rows for key-tile group gj: bit r = route row rr0 + r.
-// The words are read through the constant address space (scalar loads).
+// The words are read through the constant address space (scalar loads); the kernel uses this for
+// the first two tiles, before its loop.
 __device__ __forceinline__ uint32_t group_bits(const const_u64* wrow, int wpr, int nrr, int gj) {
   uint32_t bits = 0;
   const int wi = gj >> 6, sh = gj & 63;
@@ -684,8 +685,16 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
     __builtin_amdgcn_sched_group_barrier(0x008, 4 * (D / 32), 0);
     if constexpr (F16S) wv.round_state_fp16();
   };
+  // Route words of later routing groups: lane r < nrr loads route row r's word with a vector load
+  // at the top of the iteration before the group starts, and a ballot of the bits forms the
+  // group's route bits at the end of it, so no scalar-load wait sits in the loop.
+  const uint64_t* wrow_v = reinterpret_cast<const uint64_t*>(a.words) +
+                           (static_cast<int64_t>(hk) * a.total_mtiles + mt0 + rr0 + min(lane, nrr - 1)) * a.wpr;
+  uint64_t word2 = 0;
   for (int n = 0; n < n_tiles; ++n) {
     dma_barrier();  // tile n landed; the K / factor stages of tile n-1 and the V^T stage of n-2 are free
+    const bool fetch = pos2 == 0 && n + 2 < n_tiles;  // tile n+2 starts a routing group (uniform)
+    if (fetch) word2 = wrow_v[grp2 >> 6];
     if constexpr (SYNC) {
       stg.k_next(kbuf, rb0 != full, rb0 != 0u);
       stg.v_next(vbuf + vs_cur * L::VSTAGE);
@@ -732,7 +741,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
     vs_next = vs_free;
     rb0 = rb1;
     // tile n+2's position in its routing group, kept as a counter (no division per tile)
-    if (pos2 == 0 && n + 2 < n_tiles) rb1 = group_bits(wrow, a.wpr, nrr, grp2);
+    if (fetch)
+      rb1 = static_cast<uint32_t>(__builtin_amdgcn_ballot_w64(lane < nrr && ((word2 >> (grp2 & 63)) & 1u) != 0u));
     if (++pos2 == tpg) {
       pos2 = 0;
       ++grp2;
