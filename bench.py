@@ -192,26 +192,48 @@ def int8_pair_counts(w):
     return n8
 
 
-SAMPLE_PAIRS = 8e8  # legal (row, head, key) triples of the oracle's sample: about 10 s of host time
+SAMPLE_PAIRS = 1e9  # legal (row, head, key) triples of the oracle's sample: about 15 s of host time
+
+
+def _sample_rows(w, local, lens, stride, k):
+    """k query rows per route row, evenly spaced from its first to its last row (offsets
+    round(i (BM_r - 1) / (k - 1))), for every stride-th route row and the last one."""
+    tiles = list(range(0, w.total_mtiles, stride))
+    if tiles[-1] != w.total_mtiles - 1:
+        tiles.append(w.total_mtiles - 1)
+    offs = sorted(set(int(round(i * (w.bm_r - 1) / (k - 1))) for i in range(k)))
+    rows = np.array(sorted(set(m * w.bm_r + o for m in tiles for o in offs if m * w.bm_r + o < w.total)),
+                    dtype=np.int64)
+    keys = local[rows] + 1 if w.causal else lens[rows]
+    return rows, int(keys.sum()) * w.hq
 
 
 def baseline_rows(w):
-    """Query rows (global token indices) of the oracle's sample: tokens BM_r m + 0, BM_r/3,
-    2 BM_r/3 and BM_r - 1 for every stride-th m below the route-row count (and the last m), the
-    stride doubled from 1 until the sample holds at most SAMPLE_PAIRS legal pairs."""
+    """Query rows (global token indices) of the oracle's sample and how they were chosen.
+    Returns (rows, stride, k): k rows per route row, evenly spaced from its first to its last
+    row, for every stride-th route row and the last one. Start from 4 rows at stride 1. When that
+    sample holds at most SAMPLE_PAIRS legal pairs, k grows (6, 8, 12, 16, 24, ... up to BM_r,
+    i.e. every row) while the sample stays within the budget; otherwise the stride doubles until
+    it fits."""
     starts = np.repeat(np.asarray(w.cu_seqlens[:-1], dtype=np.int64), np.diff(w.cu_seqlens))
     local = np.arange(w.total, dtype=np.int64) - starts  # sequence-local index of every token
     lens = np.repeat(np.diff(w.cu_seqlens), np.diff(w.cu_seqlens))
-    stride = 1
+    k = min(4, w.bm_r)
+    rows, pairs = _sample_rows(w, local, lens, 1, k)
+    if pairs <= SAMPLE_PAIRS:
+        while k < w.bm_r:
+            k_next = min(w.bm_r, k * 3 // 2 if k & (k - 1) == 0 else k * 4 // 3)  # 4, 6, 8, 12, 16, 24, ...
+            r2, p2 = _sample_rows(w, local, lens, 1, k_next)
+            if p2 > SAMPLE_PAIRS:
+                break
+            rows, k = r2, k_next
+        return rows, 1, k
+    stride = 2
     while True:
-        tiles = list(range(0, w.total_mtiles, stride))
-        if tiles[-1] != w.total_mtiles - 1:
-            tiles.append(w.total_mtiles - 1)
-        rows = [m * w.bm_r + off for m in tiles for off in (0, w.bm_r // 3, (2 * w.bm_r) // 3, w.bm_r - 1)]
-        rows = np.array(sorted(set(x for x in rows if x < w.total)), dtype=np.int64)
-        keys = local[rows] + 1 if w.causal else lens[rows]
-        if int(keys.sum()) * w.hq <= SAMPLE_PAIRS or len(tiles) <= 2:
-            return rows, stride
+        rows, pairs = _sample_rows(w, local, lens, stride, k)
+        n_tiles = len(range(0, w.total_mtiles, stride)) + 1
+        if pairs <= SAMPLE_PAIRS or n_tiles <= 2:
+            return rows, stride, k
         stride *= 2
 
 
@@ -235,7 +257,7 @@ def oracle_problem(w, scale_blocks=None):
                            q_scale=qs, k8=k8, k_scale=ks, kv_int8=w.kv_int8, **extra)
 
 
-def cpu_baseline(w, prob, rows, stride, scale_blocks=None):
+def cpu_baseline(w, prob, rows, stride, per_tile, scale_blocks=None):
     import oracle
     prep = oracle_problem(w, scale_blocks)
     t0 = time.perf_counter()
@@ -250,9 +272,9 @@ def cpu_baseline(w, prob, rows, stride, scale_blocks=None):
         "unit": "TFLOP/s",
         "cores": oracle.max_threads(),
         "kind": "oracle",
-        "sample": f"{len(rows)} query rows x {w.hq} heads (tokens {w.bm_r} m + 0, {w.bm_r // 3}, "
-                  f"{2 * w.bm_r // 3}, {w.bm_r - 1} for m = 0, {stride}, {2 * stride}, ... and the last m; "
-                  f"{nall} legal pairs), fp64 oracle, {dt:.1f} s",
+        "sample": f"{len(rows)} query rows x {w.hq} heads ({per_tile} rows per {w.bm_r}-row route tile, "
+                  f"evenly spaced from its first to its last row, for route tiles m = 0, {stride}, "
+                  f"{2 * stride}, ... and the last one; {nall} legal pairs), fp64 oracle, {dt:.1f} s",
         "seconds": dt,
         "parity_max_abs_err_on_sample": err,
     }
@@ -798,8 +820,8 @@ def main():
     }
     result["context"] = PAGES_CONTEXT
     if not args.no_cpu_baseline:
-        rows, stride = baseline_rows(w)
-        result["cpu_baseline"] = cpu_baseline(w, prob, rows, stride, args.scale_blocks)
+        rows, stride, per_tile = baseline_rows(w)
+        result["cpu_baseline"] = cpu_baseline(w, prob, rows, stride, per_tile, args.scale_blocks)
     print(json.dumps(result), flush=True)
 
 

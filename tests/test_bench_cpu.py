@@ -21,7 +21,7 @@ def legal_keys(w, rows):
 @pytest.mark.parametrize("name", ["tiny", "mha8k", "gqa32k", "varlen64k"])
 def test_baseline_rows_sample(name):
     w = wl.make(name)
-    rows, stride = bench.baseline_rows(w)
+    rows, stride, k = bench.baseline_rows(w)
     assert rows.dtype == np.int64 and rows.ndim == 1 and len(rows) > 0
     assert np.all(np.diff(rows) > 0), "rows sorted and unique"
     assert rows[0] == 0 and rows[-1] < w.total
@@ -29,6 +29,7 @@ def test_baseline_rows_sample(name):
     pairs = int(legal_keys(w, rows).sum()) * w.hq
     assert pairs <= bench.SAMPLE_PAIRS
     assert stride >= 1 and stride & (stride - 1) == 0
+    assert 4 <= k <= w.bm_r and (stride == 1 or k == 4)
 
 
 def shape_only(seqlens, hq, bm_r=128, causal=True):
@@ -40,10 +41,24 @@ def shape_only(seqlens, hq, bm_r=128, causal=True):
 
 
 def test_baseline_rows_stride_grows_with_size():
-    _, s_small = bench.baseline_rows(shape_only([8192], 32))
-    rows, s_big = bench.baseline_rows(shape_only([131072], 32))
-    assert s_small == 1 and s_big > 1
+    _, s_small, k_small = bench.baseline_rows(shape_only([8192], 32))
+    rows, s_big, k_big = bench.baseline_rows(shape_only([131072], 32))
+    assert s_small == 1 and s_big > 1 and k_big == 4
     assert int(legal_keys(shape_only([131072], 32), rows).sum()) * 32 <= bench.SAMPLE_PAIRS
+
+
+def test_baseline_rows_fill_the_budget():
+    # a small workload is sampled in full; a mid-size one takes more rows per route tile, close to
+    # the budget, before any stride is used
+    w = shape_only([300, 77], 4, bm_r=64)
+    rows, stride, k = bench.baseline_rows(w)
+    assert stride == 1 and k == 64 and np.array_equal(rows, np.arange(377))
+    w = shape_only([32768], 32)
+    rows, stride, k = bench.baseline_rows(w)
+    pairs = int(legal_keys(w, rows).sum()) * 32
+    assert stride == 1 and k > 4 and 0.5 * bench.SAMPLE_PAIRS < pairs <= bench.SAMPLE_PAIRS
+    offs = sorted(set(int(r) % 128 for r in rows))
+    assert offs[0] == 0 and offs[-1] == 127 and len(offs) == k
 
 
 def test_int8_pair_counts_closed_forms():
