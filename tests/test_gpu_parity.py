@@ -148,6 +148,11 @@ SMALL = [
     dict(seqlens=[1000], hq=4, hk=4, d=128, bm_r=256, bn_r=192, group=1),
     dict(seqlens=[700, 333], hq=4, hk=1, d=128, bm_r=64, bn_r=64, group=1, kv_int8=True),
     dict(seqlens=[160], hq=2, hk=2, d=64, bm_r=32, bn_r=64, group=1, kv_int8=True, causal=False),
+    # route tiles that do not divide the 256-row workgroup: 3 or 4 route rows per workgroup at
+    # varying offsets, a route tile taller than the workgroup, two route words per row
+    dict(seqlens=[700, 300], hq=4, hk=2, d=128, bm_r=96, bn_r=64, group=2),
+    dict(seqlens=[600, 31], hq=2, hk=1, d=64, bm_r=288, bn_r=128, group=1),
+    dict(seqlens=[4500], hq=2, hk=1, d=64, bm_r=160, bn_r=64, group=1),
 ]
 
 
