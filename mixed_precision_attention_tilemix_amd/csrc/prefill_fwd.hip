@@ -9,7 +9,11 @@
 //     sequence; grid = (query heads, query tiles in reverse order, sequences). Heads vary
 //     fastest and are ordered so that consecutive workgroups (which the hardware deals out to
 //     the 8 XCDs in turn) keep the query heads of one KV head on one XCD and its L2, and the
-//     heaviest causal tiles start first.
+//     heaviest causal tiles start first. With a multiple of 8 KV heads and 64 or more query
+//     tiles, each XCD instead works through its KV heads one at a time (all query tiles of one,
+//     heaviest first, then the next), so that the workgroups in flight on an XCD share one KV
+//     head's tiles in its L2 rather than several; with one KV head per XCD (8 KV heads) the two
+//     orders are the same.
 //   * each wavefront owns 32 query rows and computes TRANSPOSED score tiles S^T = K Q^T with
 //     32x32 MFMAs, so the accumulator lands in the B-operand layout of O^T += V^T P^T: lane l
 //     holds query l%32. Key rows inside each 32-key block are loaded in a permuted order (bits 2
@@ -549,10 +553,23 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
   // XCD-friendly head order: consecutive workgroups cycle through the KV heads first
   const int x = blockIdx.x;
   const int grp = a.hq / a.hkv;
-  const int h = grp * (x % a.hkv) + x / a.hkv;
   const int b = blockIdx.z;
   const int n_ct = (a.max_seqlen_q + BM - 1) / BM;
-  const int c = n_ct - 1 - static_cast<int>(blockIdx.y);
+  int h, c;
+  if (a.hkv % 8 == 0 && n_ct >= 64) {
+    // long sequences, KV heads a multiple of 8: workgroup lin of a sequence runs on XCD lin % 8,
+    // which takes its KV heads j, j + 8, ... one at a time: the k-th workgroup it receives is
+    // query tile c (heaviest first) of query head r % grp of its KV head k / (grp n_ct)
+    const int lin = x + a.hq * static_cast<int>(blockIdx.y);
+    const int j = lin & 7, k = lin >> 3;
+    const int per_kv = grp * n_ct;
+    const int r = k % per_kv;
+    c = n_ct - 1 - r / grp;
+    h = (j + 8 * (k / per_kv)) * grp + r % grp;
+  } else {
+    h = grp * (x % a.hkv) + x / a.hkv;
+    c = n_ct - 1 - static_cast<int>(blockIdx.y);
+  }
   const int q_begin = ld_uniform(a.cu_q, b);
   const int Lq = ld_uniform(a.cu_q, b + 1) - q_begin;
   const int k_begin = ld_uniform(a.cu_k, b);

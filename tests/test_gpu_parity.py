@@ -382,6 +382,22 @@ def test_mha8k_full_output_parity():
           f"(fused Q, fp16 out), INT8 pairs {n8 / nall:.3f}")
 
 
+def test_long_mha_head_order_parity():
+    """A 16k multi-head (8 = 8 KV heads) sequence: 64 query tiles, so each XCD takes its KV heads
+    one at a time. Sampled rows of every head against the oracle, in the configuration bench.py
+    times."""
+    w = wl.custom([16384], 8, 8, 64, bm_r=128, bn_r=128, group=1, p_fp16=0.25, seed=27)
+    rows = sample_rows(w, n_random=96)
+    ref, ref_lse, _, _ = oracle.prepare(w).prefill(rows)
+    idx = torch.from_numpy(rows).cuda()
+    prob = DeviceProblem(w, out_dtype=torch.float16, fused_q=True)
+    prob.step()
+    torch.cuda.synchronize()
+    err = check_out(prob.out[idx].float().cpu().numpy(), ref, "mha16k", fp16_out=True)
+    check_lse(prob.lse[:, idx].cpu().numpy(), ref_lse, "mha16k")
+    print(f"mha16k (8 heads): {len(rows)} rows, max err {err:.2e}")
+
+
 def route_row_edges(w):
     """The first and the last query row of every route row of every sequence."""
     rows = set()
