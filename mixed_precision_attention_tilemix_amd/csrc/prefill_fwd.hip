@@ -670,7 +670,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
   uint32_t rb1 = n_tiles > 1 ? bits_of(1) : 0u;
   int pos2 = 2 % tpg, grp2 = 2 / tpg;  // routing group of tile 2 and the tile's place in it
 
-  // fused Q quantization: each lane quantizes its half of its query row from the fp16 tile in LDS
+  // fused Q quantization: each lane quantizes its half of its query row from its fp16 fragments
   if (a.q8 == nullptr) {
     const float qs = quantize_q_regs<D>(wv.q16f, hl, wv.q8f);  // every lane: exchanges with lane ^ 32
     if (wv.row_valid) wv.cq = fmaxf(qs * a.scale_log2, 1e-30f);
