@@ -179,6 +179,12 @@ typedef struct tilemix_fwd_params {
    * stay as without it. The row max is held in log2 units, so |max score| * log2(e) must stay
    * below 65504. 0 keeps fp32 state. Prefill only: tilemix_decode_fwd rejects it. */
   int32_t state_fp16;
+  /* How the fused prefill kernel reads V (results are identical either way): 1 = a pre-pass
+   * writes V transposed into the workspace, tile by tile; 2 = the kernel stages V rows as they
+   * are and transposes them with its LDS reads (no pre-pass, no workspace without kv_int8);
+   * 0 = the library chooses (2 when the V pre-pass would be a sizable share of the call: short
+   * sequences relative to the number of KV heads, 1 otherwise). Prefill only; decode ignores it. */
+  int32_t v_path;
 } tilemix_fwd_params;
 
 /*

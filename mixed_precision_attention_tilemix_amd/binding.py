@@ -69,6 +69,7 @@ class FwdParams(ctypes.Structure):
         ("k_scale_block", ctypes.c_int32),
         ("debug_sync_stages", ctypes.c_int32),
         ("state_fp16", ctypes.c_int32),
+        ("v_path", ctypes.c_int32),
     ]
 
 
@@ -218,7 +219,7 @@ def _fwd_params(*, q, q8, q_scale, k8, k_scale, route_words, cu_seqlens_q, cu_se
                 cu_mtiles, max_seqlen_q, max_seqlen_k, route_block_m, route_block_n, route_group,
                 out, workspace, k, v, v8, v_scale, causal, softmax_scale, lse, debug_s32,
                 debug_head, debug_mtile_begin, debug_mtile_count, k_scale_block=0,
-                debug_sync_stages=False, state_fp16=False) -> FwdParams:
+                debug_sync_stages=False, state_fp16=False, v_path=0) -> FwdParams:
     kv_int8 = v8 is not None
     qs = _tok_head_strides(q)
     ks = _tok_head_strides(k) if k is not None else (0, 0)
@@ -256,6 +257,7 @@ def _fwd_params(*, q, q8, q_scale, k8, k_scale, route_words, cu_seqlens_q, cu_se
     p.k_scale_block = int(k_scale_block)
     p.debug_sync_stages = int(bool(debug_sync_stages))
     p.state_fp16 = int(bool(state_fp16))
+    p.v_path = int(v_path)
     if debug_s32 is not None:
         p.debug_head, p.debug_mtile_begin = debug_head, debug_mtile_begin
         p.debug_mtile_count, p.debug_ntiles_max = debug_mtile_count, debug_s32.shape[1]
@@ -270,7 +272,8 @@ def tilemix_prefill_fwd(*, q, q8, q_scale, k8, k_scale, route_words, cu_seqlens_
                         v_scale=None, causal: bool = True, softmax_scale: float = 0.0, lse=None,
                         debug_s32=None, debug_head: int = 0, debug_mtile_begin: int = 0,
                         debug_mtile_count: int = 0, k_scale_block: int = 0,
-                        debug_sync_stages: bool = False, state_fp16: bool = False, stream=None) -> None:
+                        debug_sync_stages: bool = False, state_fp16: bool = False, v_path: int = 0,
+                        stream=None) -> None:
     """Fill tilemix_fwd_params from device tensors and call tilemix_prefill_fwd."""
     p = _fwd_params(q=q, q8=q8, q_scale=q_scale, k8=k8, k_scale=k_scale, route_words=route_words,
                     cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k, cu_mtiles=cu_mtiles,
@@ -281,7 +284,7 @@ def tilemix_prefill_fwd(*, q, q8, q_scale, k8, k_scale, route_words, cu_seqlens_
                     debug_s32=debug_s32, debug_head=debug_head,
                     debug_mtile_begin=debug_mtile_begin, debug_mtile_count=debug_mtile_count,
                     k_scale_block=k_scale_block, debug_sync_stages=debug_sync_stages,
-                    state_fp16=state_fp16)
+                    state_fp16=state_fp16, v_path=v_path)
     _check(load().tilemix_prefill_fwd(ctypes.byref(p), _stream(stream)))
 
 

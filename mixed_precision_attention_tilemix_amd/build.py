@@ -10,7 +10,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtilemix.so")
-SOURCES = ["api.cpp", "quantize.hip", "pack.hip", "vt_pack.hip", "prefill_fwd.hip", "decode.hip", "route.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "pack.hip", "vt_pack.hip", "cache_widen.hip", "prefill_fwd.hip", "decode.hip", "route.hip"]
 PEAK_LIB = os.path.join(HERE, "libtilemix_peak.so")
 PEAK_SOURCES = ["mfma_peak.hip"]
 

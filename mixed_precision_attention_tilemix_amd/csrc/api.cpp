@@ -56,23 +56,40 @@ tilemix_status check_quant_group(const char* name, const void* x, int64_t n, int
 }
 
 struct WorkspaceLayout {
-  int64_t vt_tiles;   // V^T tile slots per KV head
-  int64_t vt_bytes;   // bytes of the V^T region
-  int64_t ks_off;     // byte offset of the per-key K scales (one fp32 per key of every tile)
-  int64_t k16_off;    // byte offset of the fp16 K copy (INT8 cache only)
+  int64_t vt_tiles;   // V^T path: V^T tile slots per KV head
+  int64_t k16_off;    // INT8 cache: byte offset of the exact fp16 K copy
+  int64_t v16_off;    // INT8 cache on the direct V path: byte offset of the dequantized fp16 V
   int64_t total;      // bytes in all
 };
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-WorkspaceLayout workspace_layout(const tilemix_fwd_params* p) {
+// V^T path: the V^T tiles, then (INT8 cache) the fp16 K copy. Direct path: nothing, or (INT8
+// cache) the fp16 K copy and the dequantized V. The V^T path never needs less.
+WorkspaceLayout workspace_layout(const tilemix_fwd_params* p, bool v_direct) {
   WorkspaceLayout w{};
-  w.vt_tiles = tilemix::key_tiles_bound(p->total_k, p->batch);
-  w.vt_bytes = round_up(static_cast<int64_t>(p->hkv) * w.vt_tiles * tilemix::kKeyTile * p->head_dim * 2, 256);
-  w.ks_off = w.vt_bytes;
-  w.k16_off = w.ks_off + round_up(static_cast<int64_t>(p->hkv) * w.vt_tiles * tilemix::kKeyTile * 4, 256);
-  w.total = w.k16_off + (p->kv_int8 ? round_up(p->total_k * p->hkv * p->head_dim * 2, 256) : 0);
+  const int64_t copy = p->kv_int8 ? round_up(p->total_k * p->hkv * p->head_dim * 2, 256) : 0;
+  if (v_direct) {
+    w.k16_off = 0;
+    w.v16_off = copy;
+    w.total = 2 * copy;
+  } else {
+    w.vt_tiles = tilemix::key_tiles_bound(p->total_k, p->batch);
+    w.k16_off = round_up(static_cast<int64_t>(p->hkv) * w.vt_tiles * tilemix::kKeyTile * p->head_dim * 2, 256);
+    w.total = w.k16_off + copy;
+  }
   return w;
+}
+
+// Which V path a call takes. The V^T pre-pass reads and writes V once (about 4 bytes per key
+// row and channel); the direct path instead doubles the kernel's LDS reads of V, a cost that grows
+// with the work per key. The direct path wins while the work per key row (query-key pairs x query
+// heads / (keys x KV heads), estimated from the largest sequence) stays under 16384: measured,
+// 8k-token multi-head and GQA 4:1 sequences gain 1-5 %, 32k GQA 4:1 loses 1 %.
+bool choose_v_direct(const tilemix_fwd_params* p) {
+  if (p->v_path != 0) return p->v_path == 2;
+  const double pairs = static_cast<double>(p->total_q) * p->max_seqlen_k * (p->causal ? 0.5 : 1.0);
+  return pairs * p->hq <= 16384.0 * static_cast<double>(p->total_k) * p->hkv;
 }
 
 // Bytes of the decode workspace: per (sequence, KV head, key chunk, query row) the chunk's max,
@@ -344,7 +361,7 @@ tilemix_status tilemix_prefill_workspace_size(const tilemix_fwd_params* p, int64
   if (p->batch < 1 || p->hkv < 1 || p->total_k < 0)
     return fail(TILEMIX_EINVAL, "prefill_workspace_size: batch=%d hkv=%d total_k=%lld", p->batch, p->hkv,
                 (long long)p->total_k);
-  *bytes = workspace_layout(p).total;
+  *bytes = workspace_layout(p, false).total;  // enough for either V path
   return ok();
 }
 
@@ -363,27 +380,41 @@ tilemix_status tilemix_prefill_fwd(const tilemix_fwd_params* p, void* stream) {
   if (p->k_scale_block < 0 || p->k_scale_block % tilemix::kKeyTile)
     return fail(TILEMIX_EINVAL, "prefill_fwd: k_scale_block %d is not 0 or a multiple of %d", p->k_scale_block,
                 tilemix::kKeyTile);
-  const WorkspaceLayout ws = workspace_layout(p);
-  if (p->workspace == nullptr || !aligned(p->workspace, 256) || p->workspace_bytes < ws.total)
+  if (p->v_path < 0 || p->v_path > 2)
+    return fail(TILEMIX_EINVAL, "prefill_fwd: v_path %d (0, 1 or 2)", p->v_path);
+  const bool v_direct = choose_v_direct(p);
+  const WorkspaceLayout ws = workspace_layout(p, v_direct);
+  if (ws.total > 0 && (p->workspace == nullptr || !aligned(p->workspace, 256) || p->workspace_bytes < ws.total))
     return fail(TILEMIX_EINVAL, "prefill_fwd: workspace must be 256-byte aligned and hold %lld bytes (got %lld)",
                 (long long)ws.total, (long long)p->workspace_bytes);
   if (p->total_q == 0 || p->max_seqlen_q == 0) return ok();
 
   tilemix::FwdArgs a = fwd_args(p);
-  a.vt_ws = static_cast<_Float16*>(p->workspace);
-  a.vt = a.vt_ws;
-  a.vt_tiles = ws.vt_tiles;
-  a.ks_ws = reinterpret_cast<float*>(static_cast<char*>(p->workspace) + ws.ks_off);
-  a.ks = a.ks_ws;
-  a.k16_ws = p->kv_int8 ? reinterpret_cast<_Float16*>(static_cast<char*>(p->workspace) + ws.k16_off) : nullptr;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  a.v_direct = v_direct ? 1 : 0;
+  char* ws_base = static_cast<char*>(p->workspace);
   if (p->kv_int8) {  // the FP16-routed tiles read the exact fp16 copy of K8
+    a.k16_ws = reinterpret_cast<_Float16*>(ws_base + ws.k16_off);
     a.k = a.k16_ws;
     a.k_stride_tok = static_cast<int64_t>(p->hkv) * p->head_dim;
     a.k_stride_head = p->head_dim;
   }
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = tilemix::launch_vt_pack(a, p->batch, p->max_seqlen_k, p->head_dim, p->kv_int8 != 0, s);
-  if (e != hipSuccess) return from_hip(e, "prefill_fwd (V^T pre-pass)");
+  hipError_t e = hipSuccess;
+  if (v_direct) {
+    if (p->kv_int8) {  // P.V reads the dequantized copy of V8
+      a.v16_ws = reinterpret_cast<_Float16*>(ws_base + ws.v16_off);
+      a.v = a.v16_ws;
+      a.v_stride_tok = static_cast<int64_t>(p->hkv) * p->head_dim;
+      a.v_stride_head = p->head_dim;
+      e = tilemix::launch_cache_widen(a, p->head_dim, s);
+    }
+  } else {
+    a.vt_ws = reinterpret_cast<_Float16*>(ws_base);
+    a.vt = a.vt_ws;
+    a.vt_tiles = ws.vt_tiles;
+    e = tilemix::launch_vt_pack(a, p->batch, p->max_seqlen_k, p->head_dim, p->kv_int8 != 0, s);
+  }
+  if (e != hipSuccess) return from_hip(e, "prefill_fwd (pre-pass)");
   return from_hip(tilemix::launch_prefill(a, p->batch, p->head_dim, p->kv_int8 != 0, s), "prefill_fwd");
 }
 

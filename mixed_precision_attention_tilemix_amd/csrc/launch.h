@@ -51,21 +51,26 @@ struct FwdArgs {
   float* lse;
   int32_t* dump;
   int32_t dump_head, dump_m0, dump_mcount, dump_ntiles;
-  // workspace written by the V^T pre-pass and read by the fused kernel
-  _Float16* vt_ws;        // [hkv][vt_tiles][D][64] swizzled V^T tiles
+  // workspace written by a pre-pass and read by the fused kernel
+  _Float16* vt_ws;        // V^T path: [hkv][vt_tiles][D][64] swizzled V^T tiles
   const _Float16* vt;     // the same, read-only view
   int64_t vt_tiles;       // tile slots per KV head (>= tiles of all sequences)
-  float* ks_ws;           // [hkv][vt_tiles][64] k_scale of every key of a tile (the last key's past the end)
-  const float* ks;        // the same, read-only view
-  _Float16* k16_ws;       // INT8 cache only: exact fp16(k8) [total_k, hkv, D]
+  _Float16* k16_ws;       // INT8 cache: exact fp16(k8) [total_k, hkv, D], read as k
+  _Float16* v16_ws;       // INT8 cache on the direct V path: fp16(v_scale * v8) [total_k, hkv, D], read as v
+  int32_t v_direct;       // V rows staged as they are (else V^T tiles from the pre-pass)
   int32_t k_block;        // > 0: K scales constant over 64-key tiles (one factor per tile)
   int32_t sync_stages;    // debug instance: every staging load waited for before any compute
   int32_t state_fp16;     // online-softmax state (m, l, O) rounded to binary16 after every key tile
 };
 
-// V^T tiles (and, with an INT8 cache, fp16 K) into the workspace; must precede launch_prefill.
+// V^T path: V^T tiles (and, with an INT8 cache, fp16 K) into the workspace; must precede
+// launch_prefill.
 hipError_t launch_vt_pack(const FwdArgs& a, int32_t batch, int32_t max_seqlen_k, int32_t head_dim,
                           bool kv_int8, hipStream_t stream);
+
+// Direct V path with an INT8 cache: exact fp16 K and dequantized fp16 V into the workspace; must
+// precede launch_prefill.
+hipError_t launch_cache_widen(const FwdArgs& a, int32_t head_dim, hipStream_t stream);
 
 hipError_t launch_prefill(const FwdArgs& a, int32_t batch, int32_t head_dim, bool kv_int8,
                           hipStream_t stream);

@@ -82,8 +82,11 @@ struct Smem {
   static constexpr int K16 = 0;                   // offsets inside one K stage
   static constexpr int K8 = K16 + BN * RB16;
   static constexpr int KSTAGE = K8 + BN * RB8;
-  static constexpr int VBUF = KBUF + 2 * KSTAGE;  // three V^T stages, [D][BN] fp16 as vt_pack.hip
-  static constexpr int VSTAGE = D * BN * 2;
+  static constexpr int VBUF = KBUF + 2 * KSTAGE;  // three V stages: [BN keys][D] fp16 rows (direct
+                                                  // path) or [D][BN] V^T as vt_pack.hip writes it
+  static constexpr int RBV = D * 2;               // bytes per V row
+  static constexpr int CV = RBV / 16;
+  static constexpr int VSTAGE = BN * RBV;
   static constexpr int SBUF = VBUF + 3 * VSTAGE;  // two slots of per-key factors
   static constexpr int SSLOT = BN * 4;            // k_scale of the tile's keys
   static constexpr int BYTES = SBUF + 2 * SSLOT;
@@ -91,6 +94,10 @@ struct Smem {
   // with (row / rows-per-256-bytes) puts them on 16 distinct 16-byte bank groups.
   __device__ static int f16(int r) { return (r / (256 / RB16)) & (C16 - 1); }
   __device__ static int f8(int r) { return (r / (256 / RB8)) & (C8 - 1); }
+  // V rows are read by transposing 8-byte reads that touch 8 rows (keys 0-3 and 8-11 of a group of
+  // 16) and 64 bytes of each: XOR-ing the chunk index of row r with fv(r) moves those 64-byte
+  // pieces of rows r = 0..3 (mod 4) onto four different 64-byte bank groups.
+  __device__ static int fv(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -117,6 +124,12 @@ __device__ __forceinline__ void dma16(const char* base, uint32_t voff, char* lds
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
 }
 
+// The same with 4 bytes per lane, to lds_block + 4 * lane.
+__device__ __forceinline__ void dma4(const char* base, uint32_t voff, char* lds_block) {
+  const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)lds_block));
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" : : "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+}
+
 // Barrier after direct global->LDS loads. The memory fence of a workgroup barrier does not
 // cover the LDS writes of these loads, so each wave first waits for all of its own outstanding
 // loads (s_waitcnt with every counter at zero); after the barrier every wave's loads have landed.
@@ -131,14 +144,15 @@ __device__ __forceinline__ int perm32(int r) { return (r & 0x13) | ((r & 4) << 1
 // Direct global->LDS staging of the key-side tiles of one (sequence, KV head). Each wavefront
 // loads fixed 1 KiB blocks of every tile; the per-lane source offsets of those blocks are
 // computed once, so issuing a tile costs one address add per block.
-template <int D>
+template <int D, bool VN>
 struct Stager {
   using L = Smem<D>;
   static constexpr int R16 = 1024 / L::RB16;  // K rows per 1 KiB block
   static constexpr int R8 = 1024 / L::RB8;
   static constexpr int NB16 = BN / R16;       // blocks per K tile
   static constexpr int NB8 = BN / R8;
-  static constexpr int NBV = D * BN * 2 / 1024;
+  static constexpr int RV = 1024 / L::RBV;   // V rows per 1 KiB block
+  static constexpr int NBV = BN / RV;
   static constexpr int I16 = (NB16 + NW - 1) / NW;  // blocks per wave
   static constexpr int I8 = (NB8 + NW - 1) / NW;
   static constexpr int IV = (NBV + NW - 1) / NW;
@@ -150,32 +164,36 @@ struct Stager {
   // order, one call per tile.
   const char* k16;   // next K tile, fp16 rows
   const char* k8;    // next K tile, int8 rows
-  const char* vt;    // next V^T tile
-  const char* ks;    // factors of the next factor tile
+  const char* v;     // next V tile: fp16 rows (direct path) or the pre-pass's V^T tile
+  const char* ks;    // k_scale of the next tile's first key
   int64_t st16;      // bytes between consecutive keys, fp16 K
   int64_t st8;       // bytes between consecutive keys, int8 K
-  uint32_t o16[I16], o8[I8], ov;
+  int64_t stv;       // bytes between consecutive keys, V
+  uint32_t o16[I16], o8[I8], ov[IV];
   int w, Lk;
-  int kn;            // index of the next K tile
-  int kfull;         // K tiles [0, kfull) are whole
+  int kn, vn, sn;    // index of the next K / V / factor tile
+  int kfull;         // tiles [0, kfull) are whole
 
-  __device__ void init(const FwdArgs& a, int k_begin, int hk, int Lk_, int w_, int64_t tile0) {
+  __device__ void init(const FwdArgs& a, int k_begin, int hk, int Lk_, int w_, int64_t vt_tile0) {
     w = w_;
     Lk = Lk_;
-    kn = 0;
+    kn = vn = sn = 0;
     kfull = Lk / BN;
     st16 = a.k_stride_tok * 2;
     st8 = static_cast<int64_t>(a.hkv) * D;
+    stv = a.v_stride_tok * 2;
     k16 = reinterpret_cast<const char*>(a.k) + k_begin * st16 + hk * a.k_stride_head * 2;
     k8 = reinterpret_cast<const char*>(a.k8) + static_cast<int64_t>(k_begin) * st8 + static_cast<int64_t>(hk) * D;
-    vt = reinterpret_cast<const char*>(a.vt + tile0 * (D * BN));
-    ks = reinterpret_cast<const char*>(a.ks + tile0 * BN);
+    v = VN ? reinterpret_cast<const char*>(a.v) + k_begin * stv + hk * a.v_stride_head * 2
+           : reinterpret_cast<const char*>(a.vt + vt_tile0 * (D * BN));
+    ks = reinterpret_cast<const char*>(a.k_scale + static_cast<int64_t>(hk) * a.total_k + k_begin);
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < I16; ++i) o16[i] = off16(lane, i, BN);
 #pragma unroll
     for (int i = 0; i < I8; ++i) o8[i] = off8(lane, i, BN);
-    ov = static_cast<uint32_t>(lane * 16);
+#pragma unroll
+    for (int i = 0; i < IV; ++i) ov[i] = VN ? offv(lane, i, BN) : static_cast<uint32_t>(lane * 16);
   }
   // byte offset of the chunk that lane loads in its i-th block of a tile whose rows past `last`
   // repeat row `last`
@@ -186,6 +204,10 @@ struct Stager {
   __device__ uint32_t off8(int lane, int i, int last) const {
     const int row = (w + NW * i) * R8 + lane / L::C8;
     return static_cast<uint32_t>(min(row, last) * st8) + ((lane % L::C8) ^ L::f8(row)) * 16;
+  }
+  __device__ uint32_t offv(int lane, int i, int last) const {
+    const int row = (w + NW * i) * RV + lane / L::CV;
+    return static_cast<uint32_t>(min(row, last) * stv) + ((lane % L::CV) ^ L::fv(row)) * 16;
   }
 
   // The next K tile into stage buf: fp16 rows if need16, int8 rows if need8. Rows past the
@@ -222,19 +244,42 @@ struct Stager {
     ++kn;
   }
 
-  // The next pre-transposed V^T tile (contiguous in the workspace) into stage buf.
+  // The next V tile into stage buf. Direct path: fp16 rows, those past the sequence end repeating
+  // the last key (whose P is zero); V^T path: the pre-transposed tile, contiguous in the workspace.
   __device__ __forceinline__ void v_next(char* buf) {
     __builtin_assume(w >= 0 && w < NW);
+    if constexpr (!VN) {
 #pragma unroll
-    for (int i = 0; i < IV; ++i)
-      if (w + NW * i < NBV) dma16(vt + (w + NW * i) * 1024, ov, buf + (w + NW * i) * 1024);
-    vt += D * BN * 2;
+      for (int i = 0; i < IV; ++i)
+        if (w + NW * i < NBV) dma16(v + (w + NW * i) * 1024, ov[i], buf + (w + NW * i) * 1024);
+      v += D * BN * 2;
+      return;
+    }
+    if (__builtin_expect(vn < kfull, 1)) {
+#pragma unroll
+      for (int i = 0; i < IV; ++i)
+        if (w + NW * i < NBV) dma16(v, ov[i], buf + (w + NW * i) * 1024);
+    } else {
+      const int lane = threadIdx.x & 63;
+      const int last = Lk - 1 - vn * BN;
+#pragma unroll
+      for (int i = 0; i < IV; ++i)
+        if (w + NW * i < NBV) dma16(v, offv(lane, i, last), buf + (w + NW * i) * 1024);
+    }
+    v += BN * stv;
+    ++vn;
   }
 
-  // The 256 bytes of per-key K scales of the next tile into a factor slot.
+  // The k_scale of the next tile's 64 keys (keys past the sequence end repeat the last key's)
+  // into a 256-byte factor slot: one 4-byte direct load per lane of the last wavefront.
   __device__ __forceinline__ void s_next(char* buf) {
-    if (w == NW - 1 && (threadIdx.x & 63) < 16) dma16(ks, ov, buf);
+    if (w == NW - 1) {
+      const int lane = threadIdx.x & 63;
+      const int key = sn < kfull ? lane : min(lane, Lk - 1 - sn * BN);
+      dma4(ks, static_cast<uint32_t>(key * 4), buf);
+    }
     ks += BN * 4;
+    ++sn;
   }
 };
 
@@ -259,7 +304,7 @@ __device__ __forceinline__ uint32_t group_bits(const const_u64* wrow, int wpr, i
 // Per-wavefront registers: constants of the wave's rows and the online-softmax state. KBLK: the K
 // scales are constant over each 64-key tile (block-wise K quantization), so one factor per tile
 // is folded into the per-row factor instead of multiplying every score.
-template <int D, bool KV8, bool KBLK>
+template <int D, bool KV8, bool KBLK, bool VN>
 struct Wave {
   int hl, my_q;
   int lim;         // last legal key (sequence-local) of this lane's query
@@ -267,7 +312,8 @@ struct Wave {
   uint64_t valid_lanes;  // wave-uniform ballot of row_valid
   // LDS byte offsets of this lane's operand rows: chunk (2*i + hl) ^ f of a row whose length is a
   // multiple of 128 bytes sits at row_start + 16*(hl ^ f) XOR 32*i, since 2*i + hl = 2*i ^ hl
-  int kbase8, vbase;      // K8 row (i = ks), V^T row (i = 16-key step)
+  int kbase8, vbase;      // K8 row (i = ks), V^T row (i = 16-key step; V^T path)
+  int vofs[D / 32];       // direct path: byte offset of this lane's transposing V read, per 32-channel block
   int kbase16;            // fp16 K row (i = ks)
   int fkey;               // key (within a 32-key half) whose factor this lane loads for its row
   int4v q8f[D / 32];
@@ -321,14 +367,29 @@ struct Wave {
     s[1] = a1;
   }
 
-  // The V^T fragments of key half KB of the tile in stage vst.
+  // The V^T fragments of key half KB of the tile in stage vst (the A operand of the P.V MFMA:
+  // lane l needs channel 32 dblk + l % 32 of keys 32 KB + 16 g8 + 8 (l / 32) + 0..7). V^T path:
+  // one 16-byte read; direct path: two transposing reads of 4 keys each from the key-major rows.
   template <int KB>
   __device__ __forceinline__ void load_v(const char* vst, half8v (&vf)[2][D / 32]) const {
+    if constexpr (!VN) {  // one 16-byte read per fragment from the V^T rows
+#pragma unroll
+      for (int g8 = 0; g8 < 2; ++g8)
+#pragma unroll
+        for (int dblk = 0; dblk < D / 32; ++dblk)
+          vf[g8][dblk] = *reinterpret_cast<const half8v*>(vst + dblk * 32 * (BN * 2) + (vbase ^ (32 * (2 * KB + g8))));
+      return;
+    }
 #pragma unroll
     for (int g8 = 0; g8 < 2; ++g8)
 #pragma unroll
-      for (int dblk = 0; dblk < D / 32; ++dblk)
-        vf[g8][dblk] = *reinterpret_cast<const half8v*>(vst + dblk * 32 * (BN * 2) + (vbase ^ (32 * (2 * KB + g8))));
+      for (int dblk = 0; dblk < D / 32; ++dblk) {
+        const char* p = vst + vofs[dblk] + (32 * KB + 16 * g8) * (2 * D);
+        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(p));
+        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(p + 4 * (2 * D)));
+        const int2v l2 = __builtin_bit_cast(int2v, lo), h2 = __builtin_bit_cast(int2v, hi);
+        vf[g8][dblk] = __builtin_bit_cast(half8v, int4v{l2[0], l2[1], h2[0], h2[1]});
+      }
   }
 
   // O^T += V^T P^T for key half KB from fragments already in registers.
@@ -535,7 +596,7 @@ __device__ __forceinline__ float quantize_q_regs(const half8v (&q16f)[D / 16], i
 //   kF16s  rounds the online-softmax state (m, l and O) to binary16 after every 64-key tile.
 enum Variant : int { kProd = 0, kDump = 1, kKblk = 2, kSync = 3, kF16s = 4 };
 
-template <int D, bool KV8, int VAR>
+template <int D, bool KV8, int VAR, bool VN>
 __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a) {
   constexpr bool DUMP = VAR == kDump;
   constexpr bool KBLK = VAR == kKblk;
@@ -599,15 +660,16 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
                           (static_cast<int64_t>(hk) * a.total_mtiles + mt0 + rr0) * a.wpr;
   const int tpg = (a.bn_r / BN) * a.group;  // pipeline tiles per routing bit
 
-  Stager<D> stg;
-  int tiles_before = 0;  // 64-key tiles of the sequences before b (tiles never straddle sequences)
-  for (int i = 0; i < b; ++i) tiles_before += (ld_uniform(a.cu_k, i + 1) - ld_uniform(a.cu_k, i) + BN - 1) / BN;
+  Stager<D, VN> stg;
+  int tiles_before = 0;  // V^T path: 64-key tiles of the sequences before b (tiles never straddle sequences)
+  if (!VN)
+    for (int i = 0; i < b; ++i) tiles_before += (ld_uniform(a.cu_k, i + 1) - ld_uniform(a.cu_k, i) + BN - 1) / BN;
   stg.init(a, k_begin, hk, Lk, w, static_cast<int64_t>(hk) * a.vt_tiles + tiles_before);
   char* const kbuf = smem + L::KBUF;
   char* const vbuf = smem + L::VBUF;
   char* const sbuf = smem + L::SBUF;
 
-  Wave<D, KV8, KBLK> wv;
+  Wave<D, KV8, KBLK, VN> wv;
   wv.hl = hl;
   wv.my_q = qa + r32;
   wv.lim = a.causal ? min(Lk - 1, wv.my_q + off) : Lk - 1;
@@ -618,6 +680,15 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
     wv.kbase16 = kr * L::RB16 + 16 * (hl ^ L::f16(kr));
     wv.kbase8 = kr * L::RB8 + 16 * (hl ^ L::f8(kr));
     wv.vbase = r32 * (BN * 2) + 16 * (hl ^ vt_swizzle(r32));
+    // transposing V reads: lane m of 16-lane group g supplies key row 8 (g >> 1) + (m >> 2) and
+    // channels 16 (g & 1) + 4 (m & 3) .. + 3, and receives channel 16 (g & 1) + m of 4 keys
+    const int g = lane >> 4, m = lane & 15;
+    const int vrow = 8 * (g >> 1) + (m >> 2);
+#pragma unroll
+    for (int dblk = 0; dblk < D / 32; ++dblk) {
+      const int chunk = 4 * dblk + 2 * (g & 1) + ((m & 3) >> 1);  // 16-byte chunk of the channels
+      wv.vofs[dblk] = vrow * L::RBV + (chunk ^ L::fv(vrow)) * 16 + 8 * (m & 1);
+    }
     wv.fkey = 16 * ((lane & 15) >> 3) + 8 * hl + (lane & 7);
   }
 
@@ -800,25 +871,29 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
         l_row > 0.0f ? (wv.m_use + log2f(l_row)) * 0.69314718055994531f : -INFINITY;
 }
 
+template <int D, bool KV8, bool VN>
+hipError_t launch_v(const FwdArgs& a, dim3 grid, hipStream_t stream) {
+  // the debug dump of the INT8 accumulators is compiled into a separate instance of the kernel
+  // (with the dump the per-key instance runs: block-wise scales are per-key scales too)
+  if (a.dump != nullptr)
+    prefill_fwd_kernel<D, KV8, kDump, VN><<<grid, dim3(NW * 64), 0, stream>>>(a);
+  else if (a.sync_stages)
+    prefill_fwd_kernel<D, KV8, kSync, VN><<<grid, dim3(NW * 64), 0, stream>>>(a);
+  else if (a.state_fp16)
+    prefill_fwd_kernel<D, KV8, kF16s, VN><<<grid, dim3(NW * 64), 0, stream>>>(a);
+  else if (a.k_block > 0)
+    prefill_fwd_kernel<D, KV8, kKblk, VN><<<grid, dim3(NW * 64), 0, stream>>>(a);
+  else
+    prefill_fwd_kernel<D, KV8, kProd, VN><<<grid, dim3(NW * 64), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
 template <int D, bool KV8>
 hipError_t launch_t(const FwdArgs& a, int32_t batch, hipStream_t stream) {
   const int n_ct = (a.max_seqlen_q + BM - 1) / BM;
   if (n_ct == 0 || batch == 0) return hipSuccess;
   dim3 grid(static_cast<unsigned>(a.hq), static_cast<unsigned>(n_ct), static_cast<unsigned>(batch));
-  // the debug dump of the INT8 accumulators is compiled into a separate instance of the kernel
-  // (with the dump the per-key instance runs: block-wise scales are per-key scales too)
-  // (the per-key instances also serve block-wise K scales: each key's scale is its block's)
-  if (a.dump != nullptr)
-    prefill_fwd_kernel<D, KV8, kDump><<<grid, dim3(NW * 64), 0, stream>>>(a);
-  else if (a.sync_stages)
-    prefill_fwd_kernel<D, KV8, kSync><<<grid, dim3(NW * 64), 0, stream>>>(a);
-  else if (a.state_fp16)
-    prefill_fwd_kernel<D, KV8, kF16s><<<grid, dim3(NW * 64), 0, stream>>>(a);
-  else if (a.k_block > 0)
-    prefill_fwd_kernel<D, KV8, kKblk><<<grid, dim3(NW * 64), 0, stream>>>(a);
-  else
-    prefill_fwd_kernel<D, KV8, kProd><<<grid, dim3(NW * 64), 0, stream>>>(a);
-  return hipGetLastError();
+  return a.v_direct ? launch_v<D, KV8, true>(a, grid, stream) : launch_v<D, KV8, false>(a, grid, stream);
 }
 
 }  // namespace

@@ -1,12 +1,8 @@
-// Pre-pass of the fused prefill: every 64-key tile of V is written transposed ([head_dim][64]),
-// in the chunk-swizzled order the fused kernel keeps in LDS, so that the kernel streams each
-// V^T tile as one contiguous block and feeds the P.V product with single 16-byte LDS reads.
-// With an INT8 K/V cache the same pass dequantizes V (fp16(v_scale * v8)) and widens K8 to an
-// exact fp16 copy for the FP16-routed tiles. HBM-bound: one read and one write of V (and K).
-//
-// The same pass gathers the k_scale of every key of the tile into one 256-byte block (keys past
-// the sequence end repeat the last key's), which the fused kernel fetches with one direct load
-// per tile and multiplies into the converted INT8 dot products.
+// Pre-pass of the fused prefill on its V^T path: every 64-key tile of V is written transposed
+// ([head_dim][64]), in the chunk-swizzled order the fused kernel keeps in LDS, so that the kernel
+// streams each V^T tile as one contiguous block and feeds the P.V product with single 16-byte LDS
+// reads. With an INT8 K/V cache the same pass dequantizes V (fp16(v_scale * v8)) and widens K8 to
+// an exact fp16 copy for the FP16-routed tiles. HBM-bound: one read and one write of V (and K).
 #include "device_types.h"
 #include "launch.h"
 #include "tile_layout.h"
@@ -56,10 +52,6 @@ __global__ __launch_bounds__(256) void vt_pack_kernel(const FwdArgs a) {
   __syncthreads();
 
   const int64_t slot = static_cast<int64_t>(hk) * a.vt_tiles + key_tiles_before(a.cu_k, b) + n;
-  if (tid < T) {
-    const int64_t tk = k_begin + min(j0 + tid, Lk - 1);
-    a.ks_ws[slot * T + tid] = a.k_scale[static_cast<int64_t>(hk) * a.total_k + tk];
-  }
   _Float16* out = a.vt_ws + slot * (D * T);
   for (int ch = tid; ch < D * (T / 8); ch += 256) {
     const int d = ch / (T / 8), pos = ch % (T / 8);

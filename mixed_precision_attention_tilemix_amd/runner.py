@@ -131,7 +131,7 @@ class DeviceProblem:
 
     def attention(self, stream=None, debug_s32: Optional[torch.Tensor] = None, debug_head: int = 0,
                   debug_mtile_begin: int = 0, debug_mtile_count: int = 0,
-                  debug_sync_stages: bool = False, state_fp16: bool = False):
+                  debug_sync_stages: bool = False, state_fp16: bool = False, v_path: int = 0):
         w = self.w
         B.tilemix_prefill_fwd(
             q=self.q, k=self.k, v=self.v, q8=None if self.fused_q else self.q8,
@@ -144,7 +144,7 @@ class DeviceProblem:
             debug_s32=debug_s32,
             debug_head=debug_head, debug_mtile_begin=debug_mtile_begin,
             debug_mtile_count=debug_mtile_count, k_scale_block=self.k_scale_block,
-            debug_sync_stages=debug_sync_stages, state_fp16=state_fp16, stream=stream)
+            debug_sync_stages=debug_sync_stages, state_fp16=state_fp16, v_path=v_path, stream=stream)
 
     def step(self, stream=None):
         self.quantize(stream)

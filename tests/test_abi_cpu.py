@@ -86,6 +86,13 @@ def base_params():
     return p
 
 
+def int8_cache(p):
+    """Switch base_params to an INT8 K/V cache (the only prefill mode with a workspace)."""
+    p.kv_int8 = 1
+    p.k = p.v = None
+    p.v8 = p.v_scale = FAKE
+
+
 BAD_CASES = [
     ("struct_size", lambda p: setattr(p, "struct_size", 8), B.TILEMIX_EINVAL),
     ("head_dim", lambda p: setattr(p, "head_dim", 96), B.TILEMIX_EUNSUPPORTED),
@@ -102,9 +109,12 @@ BAD_CASES = [
     ("odd stride", lambda p: setattr(p, "q_stride_head", 4), B.TILEMIX_EINVAL),
     ("misaligned q", lambda p: setattr(p, "q", FAKE + 2), B.TILEMIX_EINVAL),
     ("out dtype", lambda p: setattr(p, "out_dtype", 7), B.TILEMIX_EINVAL),
-    ("null workspace", lambda p: setattr(p, "workspace", None), B.TILEMIX_EINVAL),
-    ("small workspace", lambda p: setattr(p, "workspace_bytes", 1024), B.TILEMIX_EINVAL),
-    ("misaligned workspace", lambda p: setattr(p, "workspace", FAKE + 16), B.TILEMIX_EINVAL),
+    ("null workspace", lambda p: (int8_cache(p), setattr(p, "workspace", None)), B.TILEMIX_EINVAL),
+    ("small workspace", lambda p: (int8_cache(p), setattr(p, "workspace_bytes", 1024)), B.TILEMIX_EINVAL),
+    ("misaligned workspace", lambda p: (int8_cache(p), setattr(p, "workspace", FAKE + 16)), B.TILEMIX_EINVAL),
+    ("null workspace on the V^T path", lambda p: (setattr(p, "v_path", 1), setattr(p, "workspace", None)),
+     B.TILEMIX_EINVAL),
+    ("v_path", lambda p: setattr(p, "v_path", 3), B.TILEMIX_EINVAL),
     ("debug range", lambda p: (setattr(p, "debug_s32", FAKE), setattr(p, "debug_head", 9),
                                setattr(p, "debug_ntiles_max", 2)), B.TILEMIX_EINVAL),
     ("debug ntiles", lambda p: (setattr(p, "debug_s32", FAKE), setattr(p, "debug_mtile_count", 1),
@@ -163,13 +173,15 @@ def test_workspace_size(lib):
     p = base_params()
     n = ctypes.c_int64(0)
     assert lib.tilemix_prefill_workspace_size(ctypes.byref(p), ctypes.byref(n)) == B.TILEMIX_OK
-    # hkv * (ceil(total_k / 64) + batch) tiles, each 64 x head_dim fp16 of V^T and the 64 fp32
-    # K scales of its keys
+    # enough for either V path, i.e. the V^T path's: hkv * (ceil(total_k / 64) + batch) tiles of
+    # 64 x head_dim fp16 (the direct path needs none without an INT8 cache)
     tiles = 2 * (256 // 64 + 1)
-    assert n.value == tiles * 64 * 128 * 2 + tiles * 64 * 4
+    assert n.value == tiles * 64 * 128 * 2
     p.kv_int8 = 1
     assert lib.tilemix_prefill_workspace_size(ctypes.byref(p), ctypes.byref(n)) == B.TILEMIX_OK
-    assert n.value == tiles * 64 * 128 * 2 + tiles * 64 * 4 + 256 * 2 * 128 * 2
+    # + the exact fp16 copy of K8 (total_k x hkv x head_dim); the direct path's K and V copies fit too
+    assert n.value == tiles * 64 * 128 * 2 + 256 * 2 * 128 * 2
+    assert n.value >= 2 * 256 * 2 * 128 * 2
     p.head_dim = 80
     assert lib.tilemix_prefill_workspace_size(ctypes.byref(p), ctypes.byref(n)) == B.TILEMIX_EUNSUPPORTED
     assert lib.tilemix_prefill_workspace_size(None, ctypes.byref(n)) == B.TILEMIX_EINVAL

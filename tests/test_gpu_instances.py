@@ -10,6 +10,9 @@
   * The FP16-state instance (state_fp16; the TileMix page, Section 4.3 and Appendix G.3) keeps the
     online-softmax state in binary16 between 64-key tiles. It is held to the same 2e-3 bar
     against the oracle as the production kernel, and must actually differ from it.
+  * The two ways of reading V (v_path 1: V^T tiles from a pre-pass; v_path 2: V rows staged as
+    they are and transposed by the LDS reads) give the same O and LSE bit for bit, in every
+    instance.
 """
 
 import functools
@@ -83,9 +86,60 @@ def test_sync_instance_bitwise_small(shape):
         prob = DeviceProblem(w, fused_q=fused)
         prob.quantize()
         prob.route_words()
-        prod = outputs(prob)
-        sync = outputs(prob, debug_sync_stages=True)
-        assert_bitwise(prod, sync, f"{ids(shape)} fused_q={fused}")
+        prod = outputs(prob, v_path=1)
+        for v_path in (1, 2):
+            tag = f"{ids(shape)} fused_q={fused} v_path={v_path}"
+            if v_path == 2:
+                assert_bitwise(prod, outputs(prob, v_path=2), tag + " (production against v_path=1)")
+            assert_bitwise(prod, outputs(prob, debug_sync_stages=True, v_path=v_path), tag)
+
+
+V_PATH_SHAPES = SHAPES + [
+    dict(seqlens=[700, 300], hq=4, hk=2, d=128, bm_r=96, bn_r=64, group=2),
+    dict(seqlens=[160, 65, 1], hq=2, hk=2, d=64, bm_r=32, bn_r=64, group=1, kv_int8=True, causal=False),
+]
+
+
+@pytest.mark.parametrize("shape", V_PATH_SHAPES, ids=[ids(s) for s in V_PATH_SHAPES])
+def test_v_paths_bitwise_all_instances(shape):
+    """Both V paths in the production, block-scale, dump and FP16-state instances: equal bit for
+    bit (the dump tiles too), and the automatic choice equal to both."""
+    w = wl.custom(seed=43, **shape)
+    prob = DeviceProblem(w, fused_q=True)
+    prob.quantize()
+    prob.route_words()
+    auto = outputs(prob)
+    for kw in ({}, dict(state_fp16=True)):
+        a, b = outputs(prob, v_path=1, **kw), outputs(prob, v_path=2, **kw)
+        assert_bitwise(a, b, f"{ids(shape)} {kw}")
+        if not kw:
+            assert_bitwise(auto, a, f"{ids(shape)} automatic choice")
+    ntiles = -(-max(w.seqlens) // w.bn_r) if w.seqlens else 1
+    dumps = []
+    for v_path in (1, 2):
+        d = torch.full((w.total_mtiles, max(ntiles, 1), w.bm_r, w.bn_r), SENTINEL, dtype=torch.int32, device="cuda")
+        o = outputs(prob, v_path=v_path, debug_s32=d, debug_head=w.hq - 1, debug_mtile_begin=0,
+                    debug_mtile_count=w.total_mtiles)
+        assert_bitwise(auto, o, f"{ids(shape)} dump instance v_path={v_path}")
+        dumps.append(d)
+    assert torch.equal(dumps[0], dumps[1]), f"{ids(shape)}: dumped tiles differ between V paths"
+    kb = DeviceProblem(w, fused_q=True, scale_blocks=(1, 128))
+    kb.quantize()
+    kb.route_words()
+    assert_bitwise(outputs(kb, v_path=1), outputs(kb, v_path=2), f"{ids(shape)} block-scale instance")
+
+
+@pytest.mark.parametrize("name", ["mha8k", "gqa32k"])
+def test_v_paths_bitwise_full_size(name):
+    """Whole outputs of a workload that takes the direct path (mha8k) and one that takes the V^T
+    path (gqa32k) by default, forced through the other path, in the configuration bench.py times."""
+    w = named(name)
+    prob = DeviceProblem(w, out_dtype=torch.float16, fused_q=True)
+    prob.quantize()
+    prob.route_words()
+    assert_bitwise(outputs(prob, v_path=1), outputs(prob, v_path=2), name)
+    del prob
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("name", ["gqa32k", "varlen64k"])
