@@ -798,7 +798,10 @@ def main():
         "roofline": {
             # instance 0 is the production kernel (per-key K scales), 2 the block-scale one
             "kernel": f"prefill_fwd_kernel<{w.d}, {str(bool(w.kv_int8)).lower()}, "
-                      f"{2 if prob.k_scale_block > 0 else 0}> (+ vt_pack pre-pass in the timed call)",
+                      f"{2 if prob.k_scale_block > 0 else 0}, {str(prob.v_path() == 2).lower()}>"
+                      + (" (+ vt_pack pre-pass in the timed call)" if prob.v_path() == 1 else
+                         " (+ cache_widen pre-pass in the timed call)" if w.kv_int8 else "")
+                      + f"; V path {prob.v_path()}",
             "bound": "mfma",
             "achieved": round(fwd_tflops, 2),
             "peak": round(peak_mixed, 1),

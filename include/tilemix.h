@@ -189,11 +189,22 @@ typedef struct tilemix_fwd_params {
 
 /*
  * tilemix_prefill_workspace_size - bytes of device workspace tilemix_prefill_fwd needs for
- * these parameters (only batch, hkv, head_dim, total_k and kv_int8 are read). Writes *bytes.
+ * these parameters on either V path (only batch, hkv, head_dim, total_k and kv_int8 are read):
+ * the V^T path's V^T tiles (plus, with kv_int8, the fp16 copy of K8), which also covers the
+ * direct path (none, or with kv_int8 the fp16 copies of K8 and of the dequantized V8). Writes
+ * *bytes.
  * Errors: EINVAL for NULL arguments or negative sizes, EUNSUPPORTED for head_dim other than
  * 64/128.
  */
 tilemix_status tilemix_prefill_workspace_size(const tilemix_fwd_params* params, int64_t* bytes);
+
+/*
+ * tilemix_prefill_v_path - the V path tilemix_prefill_fwd takes for these parameters: 1 (V^T
+ * pre-pass) or 2 (direct), i.e. params->v_path when it is 1 or 2, else the library's choice from
+ * total_q, total_k, max_seqlen_k, hq, hkv and causal. Returns 0 for NULL or a v_path outside
+ * 0..2. Reads nothing on the device.
+ */
+int32_t tilemix_prefill_v_path(const tilemix_fwd_params* params);
 
 /*
  * tilemix_prefill_fwd - the fused routed attention (Sections 4.1 and 4.3).
@@ -213,8 +224,10 @@ tilemix_status tilemix_prefill_workspace_size(const tilemix_fwd_params* params, 
  * when it loads it, with the same arithmetic as tilemix_quantize_qk (per-token symmetric,
  * bit-identical codes and scales), so the separate Q pass is skipped. One NULL is EINVAL.
  *
- * Implementation: a pre-pass writes V^T tiles (and, with kv_int8, fp16 K) into the workspace,
- * then the fused kernel runs; both are enqueued on `stream`.
+ * Implementation: on the V^T path (v_path) a pre-pass writes V^T tiles (and, with kv_int8, fp16
+ * K) into the workspace; on the direct path only kv_int8 has a pre-pass (fp16 K and dequantized
+ * V); then the fused kernel runs. All of it is enqueued on `stream`. With no pre-pass (direct
+ * path, fp16 K/V) the workspace is not touched and may be NULL.
  *
  * Errors: EINVAL for a NULL required pointer, struct_size mismatch, hq % hkv != 0,
  * route_block_m not a multiple of 32, route_block_n not a multiple of 64, route_group < 1,

@@ -26,7 +26,7 @@ EXPORTED = ("tilemix_last_error", "tilemix_version", "tilemix_quantize_qk",
             "tilemix_pack_route_mask", "tilemix_prefill_workspace_size", "tilemix_prefill_fwd",
             "tilemix_decode_workspace_size", "tilemix_decode_fwd", "tilemix_route_workspace_size",
             "tilemix_route_topk_maxabs", "tilemix_route_bernoulli", "tilemix_quantize_blocks",
-            "tilemix_decode_fwd_noalloc", "tilemix_decode_noalloc_max_bytes")
+            "tilemix_decode_fwd_noalloc", "tilemix_decode_noalloc_max_bytes", "tilemix_prefill_v_path")
 
 
 class TilemixError(RuntimeError):
@@ -126,6 +126,8 @@ def load(path: Optional[str] = None):
     L.tilemix_decode_fwd_noalloc.argtypes = [ctypes.POINTER(FwdParams), vp]
     L.tilemix_decode_noalloc_max_bytes.restype = i64
     L.tilemix_decode_noalloc_max_bytes.argtypes = []
+    L.tilemix_prefill_v_path.restype = ctypes.c_int32
+    L.tilemix_prefill_v_path.argtypes = [ctypes.POINTER(FwdParams)]
     for name in ("tilemix_route_topk_maxabs", "tilemix_route_bernoulli"):
         getattr(L, name).restype = ctypes.c_int
         getattr(L, name).argtypes = [ctypes.POINTER(RouteParams), vp]
@@ -331,6 +333,16 @@ def tilemix_decode_fwd_noalloc(*, q, q8, q_scale, k8, k_scale, v8, v_scale, rout
                     v_scale=v_scale, causal=causal, softmax_scale=softmax_scale, lse=lse,
                     debug_s32=None, debug_head=0, debug_mtile_begin=0, debug_mtile_count=0)
     _check(load().tilemix_decode_fwd_noalloc(ctypes.byref(p), _stream(stream)))
+
+
+def tilemix_prefill_v_path(*, total_q: int, total_k: int, max_seqlen_k: int, hq: int, hkv: int,
+                           causal: bool = True, v_path: int = 0) -> int:
+    """The V path tilemix_prefill_fwd takes for these sizes: 1 (V^T pre-pass) or 2 (direct)."""
+    p = FwdParams()
+    p.struct_size = ctypes.sizeof(FwdParams)
+    p.total_q, p.total_k, p.max_seqlen_k = total_q, total_k, max_seqlen_k
+    p.hq, p.hkv, p.causal, p.v_path = hq, hkv, int(bool(causal)), v_path
+    return int(load().tilemix_prefill_v_path(ctypes.byref(p)))
 
 
 def tilemix_decode_noalloc_max_bytes() -> int:

@@ -365,6 +365,11 @@ tilemix_status tilemix_prefill_workspace_size(const tilemix_fwd_params* p, int64
   return ok();
 }
 
+int32_t tilemix_prefill_v_path(const tilemix_fwd_params* p) {
+  if (p == nullptr || p->v_path < 0 || p->v_path > 2) return 0;
+  return choose_v_direct(p) ? 2 : 1;
+}
+
 tilemix_status tilemix_prefill_fwd(const tilemix_fwd_params* p, void* stream) {
   if (tilemix_status st = check_params(p, "prefill_fwd")) return st;
   if (p->debug_s32) {

@@ -29,15 +29,23 @@
 //   tile, then reads the V^T fragments and issues both halves' P.V MFMAs. The two wavefronts
 //   that share a SIMD (w and w + 4) take these steps in different orders: the second one runs
 //   the P.V of the previous tile before the scores of the current one, so that one tends to
-//   issue MFMAs while the other runs its softmax (V^T keeps three stages for it). Operand reads
+//   issue MFMAs while the other runs its softmax (V keeps three stages for it). Operand reads
 //   are issued ahead of their MFMAs so that each waits only for its own data: the direct loads
 //   are written as inline assembly, because the compiler counts a pending direct load against
 //   the LDS counter too and would then wait for every LDS read to finish before each MFMA. One
 //   barrier per 64-key tile; the next tile's K (fp16 and/or int8, as the route bits of the
-//   workgroup ask), V^T and per-key factors are fetched with direct global->LDS loads while the
+//   workgroup ask), V and per-key factors are fetched with direct global->LDS loads while the
 //   current tile is computed. The queries never pass through LDS: each lane keeps its row's fp16
 //   fragments (the FP16 route's B operand, 32 registers at head_dim 128) and int8 fragments in
-//   registers, which leaves LDS to the K / V^T / factor stages (96.5 KiB at head_dim 128).
+//   registers, which leaves LDS to the K / V / factor stages (96.5 KiB at head_dim 128).
+//
+// V: two paths, bitwise the same results. V^T path: a pre-pass writes every 64-key tile of V
+//   transposed and chunk-swizzled, the kernel streams it as contiguous 1 KiB blocks and reads
+//   each P.V operand fragment with one 16-byte LDS read. Direct path (no pre-pass): the kernel
+//   stages V rows as they are (chunk-swizzled on the load side) and builds each operand fragment
+//   with two transposing 8-byte LDS reads (ds_read_b64_tr_b16), twice the LDS read instructions.
+//   The host picks the direct path when the pre-pass would cost more than those reads, i.e. for
+//   short sequences.
 //
 // Softmax
 //   Base 2, with the score scale folded into one FMA per element. The running max is only
@@ -50,8 +58,8 @@
 //   slow path's join merges whole registers instead of re-packing halves.
 //
 // INT8 scores
-//   The int32 accumulator is converted to fp32 and multiplied by the key's k_scale (gathered per
-//   tile by the V^T pre-pass), then one FMA with the per-row factor and the running max gives
+//   The int32 accumulator is converted to fp32 and multiplied by the key's k_scale (staged per
+//   tile from k_scale with one 4-byte direct load per lane), then one FMA with the per-row factor and the running max gives
 //   the exponent. The scales reach the multiply through a DPP row broadcast: each lane loads one
 //   scale per 32-key half and accumulator slot t takes it from lane t of its 16-lane row.
 #include <utility>
@@ -747,7 +755,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
     if (wv.row_valid) wv.cq = fmaxf(qs * a.scale_log2, 1e-30f);
   }
 
-  // ---- prologue: K, V^T and factors of tile 0 (the single-buffered instance loads every tile in
+  // ---- prologue: K, V and factors of tile 0 (the single-buffered instance loads every tile in
   // its own iteration)
   if (!SYNC && n_tiles > 0) {
     stg.k_next(kbuf, rb0 != full, rb0 != 0u);
@@ -759,10 +767,10 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
   // two wavefronts that share a SIMD (w and w + NW/2) take the tile's steps in different orders:
   // wave w < NW/2 does scores, softmax and P.V of tile n; wave w >= NW/2 does the P.V of tile
   // n-1 first, then the scores and softmax of tile n (its P.V follows in iteration n+1), so that
-  // one issues matrix-core work while the other runs its softmax. V^T therefore keeps three
+  // one issues matrix-core work while the other runs its softmax. V therefore keeps three
   // stages (tiles n-1, n, n+1); K and the factors keep two.
   const bool lag = w >= NW / 2;  // wave-uniform
-  int vs_prev = 2, vs_cur = 0, vs_next = 1;  // V^T stages of tiles n-1, n, n+1
+  int vs_prev = 2, vs_cur = 0, vs_next = 1;  // V stages of tiles n-1, n, n+1
   auto pv_tile = [&](const char* vst) {
     half8v va[2][D / 32], vb[2][D / 32];
     wv.template load_v<0>(vst, va);
@@ -780,7 +788,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
                            (static_cast<int64_t>(hk) * a.total_mtiles + mt0 + rr0 + min(lane, nrr - 1)) * a.wpr;
   uint64_t word2 = 0;
   for (int n = 0; n < n_tiles; ++n) {
-    dma_barrier();  // tile n landed; the K / factor stages of tile n-1 and the V^T stage of n-2 are free
+    dma_barrier();  // tile n landed; the K / factor stages of tile n-1 and the V stage of n-2 are free
     const bool fetch = pos2 == 0 && n + 2 < n_tiles;  // tile n+2 starts a routing group (uniform)
     if (fetch) word2 = wrow_v[grp2 >> 6];
     if constexpr (SYNC) {

@@ -151,6 +151,12 @@ class DeviceProblem:
         self.route_words(stream)
         self.attention(stream)
 
+    def v_path(self) -> int:
+        """The V path attention() takes by default: 1 (V^T pre-pass) or 2 (direct)."""
+        w = self.w
+        return B.tilemix_prefill_v_path(total_q=w.total, total_k=w.total, max_seqlen_k=self.max_seqlen,
+                                        hq=w.hq, hkv=w.hk, causal=w.causal)
+
 
 class DeviceDecode:
     """A decode workload in device memory: fp16 Q of the new tokens, the INT8 K/V cache

@@ -187,6 +187,25 @@ def test_workspace_size(lib):
     assert lib.tilemix_prefill_workspace_size(None, ctypes.byref(n)) == B.TILEMIX_EINVAL
 
 
+def test_v_path_choice(lib):
+    """The V path of a prefill call: the forced one, or the library's choice from the sizes (direct
+    for short sequences relative to the KV heads, V^T pre-pass for long ones)."""
+    def path(L, hq, hkv, causal=True, v_path=0, batch_total=None):
+        T = batch_total or L
+        return B.tilemix_prefill_v_path(total_q=T, total_k=T, max_seqlen_k=L, hq=hq, hkv=hkv,
+                                        causal=causal, v_path=v_path)
+    assert path(8192, 32, 32) == 2      # 8k multi-head
+    assert path(256, 2, 2) == 2         # tiny
+    assert path(32768, 32, 8) == 1      # 32k GQA 4:1
+    assert path(131072, 32, 8) == 1     # 128k
+    assert path(16384, 28, 4, batch_total=65752) == 1  # the varlen batch
+    assert path(8192, 32, 8) == 2 and path(8193, 32, 8) == 1  # the boundary: 16384 pairs per key row
+    assert path(8192, 32, 8, causal=False) == 1
+    assert path(32768, 32, 8, v_path=2) == 2 and path(256, 2, 2, v_path=1) == 1
+    assert path(256, 2, 2, v_path=3) == 0
+    assert lib.tilemix_prefill_v_path(None) == 0
+
+
 def test_version(lib):
     assert B.version() >= 100
 
