@@ -179,6 +179,17 @@ __global__ __launch_bounds__(NWV * 64, 2) void decode_chunk_kernel(const DecodeA
   }
   const int off = Lk - Lq;  // bottom-right causal alignment
 
+  // The first tile's key and value rows do not depend on the queries: their loads go out first,
+  // so that their latency overlaps the query rows' loads and quantization below. (The loads are
+  // issued unconditionally, their keys clamped to the sequence, so every path through the loop
+  // has the same loads in flight and each wait covers only older ones.)
+  const int r32 = lane & 31, hl = lane >> 5;  // this lane: query row r32 of the padded 32, key half hl
+  const int kr = perm32(r32);
+  const int jw0 = j0 + NT * TK * w;  // first key of this wavefront's tiles
+  int4v kf[KS], vr[VU];
+  float scl = 0.0f;
+  load_tile<D>(a, k_begin, Lk, jw0, hk, kr, hl, lane, kf, vr, scl);
+
   // ---- the chunk's query rows into LDS
   const bool fused_q = a.q8 == nullptr;  // quantize the query rows here instead of reading q8
   if (!fused_q) {
@@ -233,8 +244,7 @@ __global__ __launch_bounds__(NWV * 64, 2) void decode_chunk_kernel(const DecodeA
   const int rr = ld_uniform(a.cu_mtiles, b);
   const const_u64* wp = (const const_u64*)(a.words) + (static_cast<int64_t>(hk) * a.total_mtiles + rr) * a.wpr;
 
-  // this lane: query row r32 of the padded 32 (real iff r32 < R), key half hl of each 16-key step
-  const int r32 = lane & 31, hl = lane >> 5;
+  // this lane's query row r32 is real iff r32 < R
   const bool row_valid = r32 < R;
   const int lim = !row_valid ? -1 : (a.causal ? min(Lk - 1, r32 / G + off) : Lk - 1);
   int4v qb[KS];  // the INT8 score operand of this lane's row
@@ -242,23 +252,16 @@ __global__ __launch_bounds__(NWV * 64, 2) void decode_chunk_kernel(const DecodeA
   for (int ks = 0; ks < KS; ++ks) qb[ks] = row_valid ? q8s[r32][2 * ks + hl] : int4v{};
   const float cqr = row_valid ? cq[r32] : 0.0f;
   const float csr = row_valid ? a.scale_log2 : 0.0f;
-  const int kr = perm32(r32);
   // transposing V8 reads: lane m of a 16-lane group g supplies row 8 (g >> 1) + (m >> 1), bytes
   // 16 (g & 1) + 8 (m & 1); it receives channel (lane & 31) of the 8 keys 8 hl .. 8 hl + 7
   const int vsrc = (8 * hl + ((lane & 15) >> 1)) * VR + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
   int8_t* const vt = vt8[w];
-  const int jw0 = j0 + NT * TK * w;  // first key of this wavefront's tiles
 
   float16v o[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) o[i] = float16v{};
   float m = -INFINITY, l = 0.0f;
 
-  // the loads are issued unconditionally (their keys are clamped to the sequence), so every
-  // path through the loop has the same loads in flight and each wait covers only older ones
-  int4v kf[KS], vr[VU];
-  float scl = 0.0f;
-  load_tile<D>(a, k_begin, Lk, jw0, hk, kr, hl, lane, kf, vr, scl);
   float* const ts = tsc[w];
 
   for (int t = 0; t < NT; ++t) {
