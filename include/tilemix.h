@@ -232,7 +232,9 @@ int32_t tilemix_prefill_v_path(const tilemix_fwd_params* params);
  * Errors: EINVAL for a NULL required pointer, struct_size mismatch, hq % hkv != 0,
  * route_block_m not a multiple of 32, route_block_n not a multiple of 64, route_group < 1,
  * k_scale_block negative or not a multiple of 64, words_per_row < 1, kv_int8 with non-NULL
- * k/v (or without v8/v_scale), a bad debug range, a NULL, misaligned or too small workspace; EUNSUPPORTED for head_dim other than 64/128.
+ * k/v (or without v8/v_scale), fp16 strides not multiples of 8 or k / v token strides of 2^24
+ * elements or more, v_path outside 0..2, a bad debug range, a misaligned or too small workspace
+ * (or a NULL one where the V path needs one); EUNSUPPORTED for head_dim other than 64/128.
  */
 tilemix_status tilemix_prefill_fwd(const tilemix_fwd_params* params, void* stream);
 

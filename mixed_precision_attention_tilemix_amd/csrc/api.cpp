@@ -196,6 +196,9 @@ tilemix_status check_params(const tilemix_fwd_params* p, const char* fn) {
     if (i >= 2 && p->kv_int8) break;
     if (st[i] < 0 || st[i] % 8) return fail(TILEMIX_EINVAL, "%s: fp16 strides must be multiples of 8", fn);
   }
+  // the fused kernel addresses up to 64 K / V rows of a tile with 32-bit byte offsets
+  if (!p->kv_int8 && (p->k_stride_tok >= (int64_t{1} << 24) || p->v_stride_tok >= (int64_t{1} << 24)))
+    return fail(TILEMIX_EINVAL, "%s: k / v token strides must be below 2^24 elements", fn);
   if (!aligned(p->q, 16) || (p->k && !aligned(p->k, 16)) || (p->v && !aligned(p->v, 16)) ||
       (p->q8 && !aligned(p->q8, 16)) || !aligned(p->k8, 16) || (p->v8 && !aligned(p->v8, 16)) ||
       !aligned(p->out, 16) || !aligned(p->k_scale, 4) || (p->v_scale && !aligned(p->v_scale, 4)) ||

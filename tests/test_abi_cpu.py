@@ -107,6 +107,7 @@ BAD_CASES = [
     ("kv_int8 with fp16 k", lambda p: setattr(p, "kv_int8", 1), B.TILEMIX_EINVAL),
     ("fp16 without v", lambda p: setattr(p, "v", None), B.TILEMIX_EINVAL),
     ("odd stride", lambda p: setattr(p, "q_stride_head", 4), B.TILEMIX_EINVAL),
+    ("huge v token stride", lambda p: setattr(p, "v_stride_tok", 1 << 24), B.TILEMIX_EINVAL),
     ("misaligned q", lambda p: setattr(p, "q", FAKE + 2), B.TILEMIX_EINVAL),
     ("out dtype", lambda p: setattr(p, "out_dtype", 7), B.TILEMIX_EINVAL),
     ("null workspace", lambda p: (int8_cache(p), setattr(p, "workspace", None)), B.TILEMIX_EINVAL),
