@@ -25,11 +25,11 @@
 // Schedule (per wavefront, one 64-key tile per iteration)
 //   After the tile's barrier each wavefront reads all K fragments of the tile and issues the
 //   score MFMAs of both 32-key halves (two interleaved accumulator chains), reads the per-key
-//   factors, converts and exponentiates both halves (VALU) with one slow-path check for the
-//   tile, then reads the V^T fragments and issues both halves' P.V MFMAs. The two wavefronts
-//   that share a SIMD (w and w + 4) take these steps in different orders: the second one runs
-//   the P.V of the previous tile before the scores of the current one, so that one tends to
-//   issue MFMAs while the other runs its softmax (V keeps three stages for it). Operand reads
+//   factors and converts the scores, then exponentiates both halves (VALU) with the P.V MFMAs
+//   of the PREVIOUS tile (its V fragments and P kept from the last iteration) issued among
+//   those instructions, so that the wavefront's own matrix-core work overlaps its softmax; one
+//   slow-path check per tile follows. P alternates between two register sets and V keeps three
+//   LDS stages (tiles n-1, n, n+1); the last tile's P.V follows the loop. Operand reads
 //   are issued ahead of their MFMAs so that each waits only for its own data: the direct loads
 //   are written as inline assembly, because the compiler counts a pending direct load against
 //   the LDS counter too and would then wait for every LDS read to finish before each MFMA. One
@@ -62,6 +62,7 @@
 //   tile from k_scale with one 4-byte direct load per lane), then one FMA with the per-row factor and the running max gives
 //   the exponent. The scales reach the multiply through a DPP row broadcast: each lane loads one
 //   scale per 32-key half and accumulator slot t takes it from lane t of its 16-lane row.
+#include <type_traits>
 #include <utility>
 
 #include "device_types.h"
@@ -331,7 +332,7 @@ struct Wave {
   float16v o[D / 32];  // O^T accumulator
   float16v s[2];       // fp32 scores of the two key halves, in units of 1 / c[half]
   float c[2];          // per-row factor of each half to log2 units: cq (INT8) or cs (FP16)
-  half8v p[2][2];      // fp16 P of the two key halves, [half][16-key step]
+  half8v p[2][2][2];   // fp16 P of the two key halves of two tiles, [set][half][16-key step]
   float m, m_use, l;   // running max (log2 units), its finite stand-in, this lane's row sum
   bool have_max;       // wave-uniform: the first tile's slow path has run
 
@@ -401,13 +402,13 @@ struct Wave {
   }
 
   // O^T += V^T P^T for key half KB from fragments already in registers.
-  template <int KB>
+  template <int KB, int SET>
   __device__ __forceinline__ void pv_regs(const half8v (&vf)[2][D / 32]) {
 #pragma unroll
     for (int g8 = 0; g8 < 2; ++g8)
 #pragma unroll
       for (int dblk = 0; dblk < D / 32; ++dblk)
-        o[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[g8][dblk], p[KB][g8], o[dblk], 0, 0, 0);
+        o[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[g8][dblk], p[SET][KB][g8], o[dblk], 0, 0, 0);
   }
 
   // Debug dump of the raw INT8 accumulators of both halves (s holds them as bits): key j of
@@ -471,7 +472,7 @@ struct Wave {
 
   // p[KB] = fp16 exp2(s * c - m_use) of half KB; returns rs plus this lane's sum of the rounded
   // P (the second half continues the first half's sum).
-  template <int KB>
+  template <int KB, int SET>
   __device__ __forceinline__ float softmax(float rs) {
     const float ck = c[KB];
 #pragma unroll
@@ -485,8 +486,25 @@ struct Wave {
         pw[e / 2] = __builtin_bit_cast(int, h2);
         rs = __builtin_amdgcn_fdot2(h2, half2v{static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)}, rs, false);
       }
-      p[KB][g8] = __builtin_bit_cast(half8v, pw);
+      p[SET][KB][g8] = __builtin_bit_cast(half8v, pw);
     }
+    return rs;
+  }
+
+  // The softmax of both halves of the current tile (P into set SET), with the P.V MFMAs of the
+  // previous tile (P in set 1 - SET, V in stage vprev) among its instructions: the matrix core
+  // works on the previous tile while the VALU exponentiates the current one. (Placing part of
+  // the P.V inside the conversion, which is route-dependent code, made the compiler spill.)
+  template <int SET>
+  __device__ __forceinline__ float softmax_pv(const char* vprev) {
+    half8v va[2][D / 32];
+    load_v<0>(vprev, va);
+    float rs = softmax<0, SET>(0.0f);
+    pv_regs<0, 1 - SET>(va);
+    half8v vb[2][D / 32];
+    load_v<1>(vprev, vb);
+    rs = softmax<1, SET>(rs);
+    pv_regs<1, 1 - SET>(vb);
     return rs;
   }
 
@@ -494,7 +512,7 @@ struct Wave {
   // check for the tile; the slow path raises the max over both halves and recomputes both P.
   // EXACT (the FP16-state instance): the max is raised whenever a score exceeds it, as in the
   // plain online recurrence, so that P <= 1 and the row sum stays within binary16 range.
-  template <bool EXACT>
+  template <bool EXACT, int SET>
   __device__ __forceinline__ void settle_tile(float rs) {
     float mx = -INFINITY;
     if constexpr (EXACT) {
@@ -522,7 +540,7 @@ struct Wave {
         m = mx;
         m_use = mx;
       }
-      rs = softmax<1>(softmax<0>(0.0f));
+      rs = softmax<1, SET>(softmax<0, SET>(0.0f));
     }
     l += rs;
   }
@@ -763,31 +781,29 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
     stg.s_next(sbuf);
   }
 
-  // ---- main loop. Iteration n: the direct loads of tile n+1 fly while tile n is computed. The
-  // two wavefronts that share a SIMD (w and w + NW/2) take the tile's steps in different orders:
-  // wave w < NW/2 does scores, softmax and P.V of tile n; wave w >= NW/2 does the P.V of tile
-  // n-1 first, then the scores and softmax of tile n (its P.V follows in iteration n+1), so that
-  // one issues matrix-core work while the other runs its softmax. V therefore keeps three
-  // stages (tiles n-1, n, n+1); K and the factors keep two.
-  const bool lag = w >= NW / 2;  // wave-uniform
+  // ---- main loop. Iteration n: the direct loads of tile n+1 fly while tile n is computed. Each
+  // wavefront issues the score MFMAs of tile n, converts them, and runs the softmax of tile n with
+  // the P.V MFMAs of tile n-1 among its VALU instructions, so its own matrix-core work overlaps
+  // its exponentials. P alternates between two register sets (the loop is unrolled by two); V
+  // keeps three stages (tiles n-1, n, n+1), K and the factors two. Iteration 0's "tile -1" is a
+  // zeroed V stage times zero P, which adds exact zeros to O. The single-buffered instance loads
+  // K, V and the factors of tile n in its own iteration and waits for them.
   int vs_prev = 2, vs_cur = 0, vs_next = 1;  // V stages of tiles n-1, n, n+1
-  auto pv_tile = [&](const char* vst) {
-    half8v va[2][D / 32], vb[2][D / 32];
-    wv.template load_v<0>(vst, va);
-    wv.template load_v<1>(vst, vb);
-    wv.template pv_regs<0>(va);
-    wv.template pv_regs<1>(vb);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4 * (D / 32), 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 4 * (D / 32), 0);
-    if constexpr (F16S) wv.round_state_fp16();
-  };
+#pragma unroll
+  for (int i = tid * 16; i < L::VSTAGE; i += NW * 64 * 16)
+    *reinterpret_cast<int4v*>(vbuf + vs_prev * L::VSTAGE + i) = int4v{};
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int g8 = 0; g8 < 2; ++g8) wv.p[1][kb][g8] = half8v{};
   // Route words of later routing groups: lane r < nrr loads route row r's word with a vector load
   // at the top of the iteration before the group starts, and a ballot of the bits forms the
   // group's route bits at the end of it, so no scalar-load wait sits in the loop.
   const uint64_t* wrow_v = reinterpret_cast<const uint64_t*>(a.words) +
                            (static_cast<int64_t>(hk) * a.total_mtiles + mt0 + rr0 + min(lane, nrr - 1)) * a.wpr;
   uint64_t word2 = 0;
-  for (int n = 0; n < n_tiles; ++n) {
+  auto iter = [&](auto set_c, int n) {
+    constexpr int SET = decltype(set_c)::value;
     dma_barrier();  // tile n landed; the K / factor stages of tile n-1 and the V stage of n-2 are free
     const bool fetch = pos2 == 0 && n + 2 < n_tiles;  // tile n+2 starts a routing group (uniform)
     if (fetch) word2 = wrow_v[grp2 >> 6];
@@ -806,9 +822,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
       const bool i8 = (rb0 >> my_rl) & 1u;
       const int st = SYNC ? 0 : (n & 1);
       const char* kst = kbuf + st * L::KSTAGE;
-      const char* vst = vbuf + vs_cur * L::VSTAGE;
       const float* scl = reinterpret_cast<const float*>(sbuf + st * L::SSLOT);
-      if (lag && n > 0) pv_tile(vbuf + vs_prev * L::VSTAGE);
       if (i8) {
         wv.qk_i8(kst);
         if constexpr (DUMP) wv.dump_i8(j0 <= dc.act_limit ? dc.row : nullptr, j0, dc.Lk, dc.bn_r, dc.tile_stride);
@@ -828,8 +842,9 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
         wv.template mask<0>(j0);
         wv.template mask<1>(j0 + 32);
       }
-      wv.template settle_tile<F16S>(wv.template softmax<1>(wv.template softmax<0>(0.0f)));
-      if (!lag) pv_tile(vst);
+      const float rs = wv.template softmax_pv<SET>(vbuf + vs_prev * L::VSTAGE);
+      if constexpr (F16S) wv.round_state_fp16();  // the state after tile n-1
+      wv.template settle_tile<F16S, SET>(rs);
     }
     const int vs_free = vs_prev;
     vs_prev = vs_cur;
@@ -843,8 +858,26 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
       pos2 = 0;
       ++grp2;
     }
+  };
+  for (int n = 0; n < n_tiles; n += 2) {
+    iter(std::integral_constant<int, 0>{}, n);
+    if (n + 1 == n_tiles) break;
+    iter(std::integral_constant<int, 1>{}, n + 1);
   }
-  if (lag && wave_live && n_tiles > 0) pv_tile(vbuf + vs_prev * L::VSTAGE);  // P.V of the last tile
+  if (wave_live && n_tiles > 0) {  // P.V of the last tile, whose P is in set (n_tiles - 1) & 1
+    const char* vst = vbuf + vs_prev * L::VSTAGE;
+    half8v va[2][D / 32], vb[2][D / 32];
+    wv.template load_v<0>(vst, va);
+    wv.template load_v<1>(vst, vb);
+    if ((n_tiles - 1) & 1) {
+      wv.template pv_regs<0, 1>(va);
+      wv.template pv_regs<1, 1>(vb);
+    } else {
+      wv.template pv_regs<0, 0>(va);
+      wv.template pv_regs<1, 0>(vb);
+    }
+    if constexpr (F16S) wv.round_state_fp16();
+  }
 
   // ---- epilogue: O = O^T / l, LSE = (m + log2 l) * ln 2
   const float l_row = wv.l + __shfl_xor(wv.l, 32);
