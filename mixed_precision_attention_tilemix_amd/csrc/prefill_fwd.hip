@@ -673,8 +673,12 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
   const int qa = q0 + ROWS_W * w;  // first query row of this wave
   const bool wave_live = qa < Lq;
   const int qlast_w = min(qa + ROWS_W - 1, Lq - 1);
-  // tiles [0, n_full) need no legality mask for any row of this wave
+  // tiles [0, n_full) need no legality mask for any row of this wave; tiles [n_wave, n_tiles)
+  // hold no legal key for any of its rows (the far side of the workgroup's causal diagonal
+  // block). The wave computes tile n_wave (all its scores masked, P = 0), whose iteration runs
+  // the P.V of its last real tile, and skips the tiles after it: they would add exact zeros.
   const int n_full = (a.causal ? min(Lk, qa + off + 1) : Lk) / BN;
+  const int n_wave = !wave_live ? -1 : a.causal ? (max(0, min(Lk, qlast_w + off + 1)) + BN - 1) / BN : n_tiles;
 
   // route rows of the workgroup and the wave's own one
   const int mt0 = ld_uniform(a.cu_mtiles, b);
@@ -817,7 +821,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
       stg.v_next(vbuf + vs_next * L::VSTAGE);
       stg.s_next(sbuf + ((n + 1) & 1) * L::SSLOT);
     }
-    if (wave_live) {
+    if (n <= n_wave) {
       const int j0 = n * BN;
       const bool i8 = (rb0 >> my_rl) & 1u;
       const int st = SYNC ? 0 : (n & 1);
@@ -864,7 +868,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
     if (n + 1 == n_tiles) break;
     iter(std::integral_constant<int, 1>{}, n + 1);
   }
-  if (wave_live && n_tiles > 0) {  // P.V of the last tile, whose P is in set (n_tiles - 1) & 1
+  if (n_wave == n_tiles && n_tiles > 0) {  // P.V of the last tile, whose P is in set (n_tiles - 1) & 1
     const char* vst = vbuf + vs_prev * L::VSTAGE;
     half8v va[2][D / 32], vb[2][D / 32];
     wv.template load_v<0>(vst, va);
