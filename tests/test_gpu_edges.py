@@ -27,7 +27,7 @@ def _cu(lens):
     return np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
 
 
-def run_case(lq, lk, hq, hk, d, bm, bn, g, causal, kv_int8, seed):
+def run_case(lq, lk, hq, hk, d, bm, bn, g, causal, kv_int8, seed, v_path=0):
     rng = np.random.default_rng(seed)
     Tq, Tk = sum(lq), sum(lk)
     q = rng.standard_normal((Tq, hq, d)).astype(np.float16)
@@ -65,7 +65,7 @@ def run_case(lq, lk, hq, hk, d, bm, bn, g, causal, kv_int8, seed):
                           v=None if kv_int8 else t(v), v8=dv8, v_scale=dvs, route_words=words,
                           cu_seqlens_q=t(cu_q), cu_seqlens_k=t(cu_k), cu_mtiles=t(cu_m),
                           max_seqlen_q=max(lq), max_seqlen_k=max(lk), route_block_m=bm, route_block_n=bn,
-                          route_group=g, causal=causal, out=out, lse=lse, workspace=ws)
+                          route_group=g, causal=causal, out=out, lse=lse, workspace=ws, v_path=v_path)
     torch.cuda.synchronize()
     got, got_lse = out.cpu().numpy(), lse.cpu().numpy()
     err = np.abs(got.astype(np.float64) - ref).max()
@@ -96,3 +96,31 @@ def test_non_causal_unequal_lengths(kv_int8):
 
 def test_gqa_64_to_1():
     run_case([300], [300], 64, 1, 128, 64, 64, 1, True, False, seed=33)
+
+
+def draw_unequal(seed):
+    """Random varlen batch whose query and key lengths differ per sequence (deterministic)."""
+    rng = np.random.default_rng(5000 + seed)
+    n = int(rng.integers(1, 5))
+    lens = [0, 1, 31, 64, 65, 255, 256, 300, 513, 1000]
+    lq = [int(x) for x in rng.choice(lens, size=n)]
+    lk = [int(x) for x in rng.choice(lens, size=n)]
+    if sum(lq) == 0:
+        lq[0] = 97
+    if sum(lk) == 0:
+        lk[-1] = 97
+    hk = int(rng.choice([1, 2, 4]))
+    return dict(lq=lq, lk=lk, hq=hk * int(rng.choice([1, 2, 4])), hk=hk, d=int(rng.choice([64, 128])),
+                bm=32 * int(rng.integers(1, 9)), bn=64 * int(rng.integers(1, 4)), g=int(rng.integers(1, 4)),
+                causal=bool(rng.integers(0, 2)), kv_int8=bool(rng.integers(0, 2)), seed=6000 + seed)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_unequal_lengths(seed):
+    # bottom-right causal alignment with L_q > L_k (rows without a legal key) and L_q < L_k, in
+    # both V paths, which must agree bit for bit
+    c = draw_unequal(seed)
+    o1, l1, _, _ = run_case(**c, v_path=1)
+    o2, l2, _, _ = run_case(**c, v_path=2)
+    assert np.array_equal(o1.view(np.int32), o2.view(np.int32)), c
+    assert np.array_equal(l1.view(np.int32), l2.view(np.int32)), c
