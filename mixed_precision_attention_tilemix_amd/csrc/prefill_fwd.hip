@@ -360,17 +360,27 @@ struct Wave {
     s[1] = __builtin_bit_cast(float16v, a1);
   }
 
-  // FP16: the two chains interleaved, one Q fragment feeding both.
+  // FP16: the two chains interleaved, one Q fragment feeding both; the K fragments are read in
+  // batches of four 16-channel steps (eight reads) ahead of their MFMAs, as in the INT8 route.
   __device__ __forceinline__ void qk_f16(const char* kst) {
     using L = Smem<D>;
     float16v a0 = {}, a1 = {};
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const half8v qv = q16f[ks];
-      const half8v k0 = *reinterpret_cast<const half8v*>(kst + L::K16 + (kbase16 ^ (32 * ks)));
-      const half8v k1 = *reinterpret_cast<const half8v*>(kst + L::K16 + 32 * L::RB16 + (kbase16 ^ (32 * ks)));
-      a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0, qv, a0, 0, 0, 0);
-      a1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1, qv, a1, 0, 0, 0);
+    for (int bt = 0; bt < D / 64; ++bt) {
+      half8v k0[4], k1[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ks = 4 * bt + j;
+        k0[j] = *reinterpret_cast<const half8v*>(kst + L::K16 + (kbase16 ^ (32 * ks)));
+        k1[j] = *reinterpret_cast<const half8v*>(kst + L::K16 + 32 * L::RB16 + (kbase16 ^ (32 * ks)));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0[j], q16f[4 * bt + j], a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1[j], q16f[4 * bt + j], a1, 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     }
     s[0] = a0;
     s[1] = a1;
