@@ -797,8 +797,10 @@ def main():
         "quantize_gbps": round(q_bytes / (quant_ms * 1e-3) / 1e9, 1) if q_bytes else None,
         "roofline": {
             # instance 0 is the production kernel (per-key K scales), 2 the block-scale one
+            # (last template argument: persistent launch, taken on the V^T path)
             "kernel": f"prefill_fwd_kernel<{w.d}, {str(bool(w.kv_int8)).lower()}, "
-                      f"{2 if prob.k_scale_block > 0 else 0}, {str(prob.v_path() == 2).lower()}>"
+                      f"{2 if prob.k_scale_block > 0 else 0}, {str(prob.v_path() == 2).lower()}, "
+                      f"{str(prob.v_path() == 1).lower()}>"
                       + (" (+ vt_pack pre-pass in the timed call)" if prob.v_path() == 1 else
                          " (+ cache_widen pre-pass in the timed call)" if w.kv_int8 else "")
                       + f"; V path {prob.v_path()}",

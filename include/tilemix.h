@@ -152,8 +152,9 @@ typedef struct tilemix_fwd_params {
 
   /* Device scratch of at least tilemix_prefill_workspace_size() bytes, 256-byte aligned,
    * owned by the caller; its contents on entry are irrelevant and on return unspecified.
-   * It holds the transposed V tiles (and, with kv_int8, an fp16 copy of K8). Calls that
-   * share one workspace must not overlap in time. */
+   * It holds the transposed V tiles (and, with kv_int8, an fp16 copy of K8) and, on the V^T
+   * path, the fused kernel's work-queue counters. Calls that share one workspace must not
+   * overlap in time. */
   void* workspace;
   int64_t workspace_bytes;
 
@@ -190,9 +191,9 @@ typedef struct tilemix_fwd_params {
 /*
  * tilemix_prefill_workspace_size - bytes of device workspace tilemix_prefill_fwd needs for
  * these parameters on either V path (only batch, hkv, head_dim, total_k and kv_int8 are read):
- * the V^T path's V^T tiles (plus, with kv_int8, the fp16 copy of K8), which also covers the
- * direct path (none, or with kv_int8 the fp16 copies of K8 and of the dequantized V8). Writes
- * *bytes.
+ * the V^T path's V^T tiles (plus, with kv_int8, the fp16 copy of K8) and 256 bytes of work-queue
+ * counters, which also covers the direct path (none, or with kv_int8 the fp16 copies of K8 and
+ * of the dequantized V8). Writes *bytes.
  * Errors: EINVAL for NULL arguments or negative sizes, EUNSUPPORTED for head_dim other than
  * 64/128.
  */
@@ -225,9 +226,11 @@ int32_t tilemix_prefill_v_path(const tilemix_fwd_params* params);
  * bit-identical codes and scales), so the separate Q pass is skipped. One NULL is EINVAL.
  *
  * Implementation: on the V^T path (v_path) a pre-pass writes V^T tiles (and, with kv_int8, fp16
- * K) into the workspace; on the direct path only kv_int8 has a pre-pass (fp16 K and dequantized
- * V); then the fused kernel runs. All of it is enqueued on `stream`. With no pre-pass (direct
- * path, fp16 K/V) the workspace is not touched and may be NULL.
+ * K) into the workspace and zeroes the work-queue counters through which the fused kernel's
+ * workgroups (as many as the device holds at once) share out the work; on the direct path only
+ * kv_int8 has a pre-pass (fp16 K and dequantized V); then the fused kernel runs. All of it is
+ * enqueued on `stream`. With no pre-pass (direct path, fp16 K/V) the workspace is not touched
+ * and may be NULL.
  *
  * Errors: EINVAL for a NULL required pointer, struct_size mismatch, hq % hkv != 0,
  * route_block_m not a multiple of 32, route_block_n not a multiple of 64, route_group < 1,

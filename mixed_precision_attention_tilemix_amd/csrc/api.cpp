@@ -59,13 +59,15 @@ struct WorkspaceLayout {
   int64_t vt_tiles;   // V^T path: V^T tile slots per KV head
   int64_t k16_off;    // INT8 cache: byte offset of the exact fp16 K copy
   int64_t v16_off;    // INT8 cache on the direct V path: byte offset of the dequantized fp16 V
+  int64_t sched_off;  // V^T path: byte offset of the fused kernel's 8 work-queue counters
   int64_t total;      // bytes in all
 };
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-// V^T path: the V^T tiles, then (INT8 cache) the fp16 K copy. Direct path: nothing, or (INT8
-// cache) the fp16 K copy and the dequantized V. The V^T path never needs less.
+// V^T path: the V^T tiles, then (INT8 cache) the fp16 K copy, then 256 bytes for the fused
+// kernel's work-queue counters. Direct path: nothing, or (INT8 cache) the fp16 K copy and the
+// dequantized V. The V^T path never needs less.
 WorkspaceLayout workspace_layout(const tilemix_fwd_params* p, bool v_direct) {
   WorkspaceLayout w{};
   const int64_t copy = p->kv_int8 ? round_up(p->total_k * p->hkv * p->head_dim * 2, 256) : 0;
@@ -76,7 +78,8 @@ WorkspaceLayout workspace_layout(const tilemix_fwd_params* p, bool v_direct) {
   } else {
     w.vt_tiles = tilemix::key_tiles_bound(p->total_k, p->batch);
     w.k16_off = round_up(static_cast<int64_t>(p->hkv) * w.vt_tiles * tilemix::kKeyTile * p->head_dim * 2, 256);
-    w.total = w.k16_off + copy;
+    w.sched_off = w.k16_off + copy;
+    w.total = w.sched_off + 256;
   }
   return w;
 }
@@ -420,6 +423,9 @@ tilemix_status tilemix_prefill_fwd(const tilemix_fwd_params* p, void* stream) {
     a.vt_ws = reinterpret_cast<_Float16*>(ws_base);
     a.vt = a.vt_ws;
     a.vt_tiles = ws.vt_tiles;
+    // the pre-pass zeroes the counters of the fused kernel's persistent launch (it runs whenever
+    // there is a key; without one the fused kernel takes one workgroup per work item)
+    if (p->max_seqlen_k > 0) a.sched = reinterpret_cast<int32_t*>(ws_base + ws.sched_off);
     e = tilemix::launch_vt_pack(a, p->batch, p->max_seqlen_k, p->head_dim, p->kv_int8 != 0, s);
   }
   if (e != hipSuccess) return from_hip(e, "prefill_fwd (pre-pass)");

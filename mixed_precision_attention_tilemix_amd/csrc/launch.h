@@ -58,6 +58,8 @@ struct FwdArgs {
   _Float16* k16_ws;       // INT8 cache: exact fp16(k8) [total_k, hkv, D], read as k
   _Float16* v16_ws;       // INT8 cache on the direct V path: fp16(v_scale * v8) [total_k, hkv, D], read as v
   int32_t v_direct;       // V rows staged as they are (else V^T tiles from the pre-pass)
+  int32_t* sched;         // V^T path: 8 work-queue counters, zeroed by the pre-pass (persistent
+                          // launch of the fused kernel); NULL: one workgroup per work item
   int32_t k_block;        // > 0: K scales constant over 64-key tiles (one factor per tile)
   int32_t sync_stages;    // debug instance: every staging load waited for before any compute
   int32_t state_fp16;     // online-softmax state (m, l, O) rounded to binary16 after every key tile

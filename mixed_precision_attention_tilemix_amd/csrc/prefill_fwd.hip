@@ -13,7 +13,9 @@
 //     tiles, each XCD instead works through its KV heads one at a time (all query tiles of one,
 //     heaviest first, then the next), so that the workgroups in flight on an XCD share one KV
 //     head's tiles in its L2 rather than several; with one KV head per XCD (8 KV heads) the two
-//     orders are the same.
+//     orders are the same. On the V^T path the kernel is launched persistent: as many workgroups
+//     as the device holds, taking these work items from per-XCD queues (see prefill_fwd_kernel),
+//     so that the XCDs, which run at slightly different speeds, finish together.
 //   * each wavefront owns 32 query rows and computes TRANSPOSED score tiles S^T = K Q^T with
 //     32x32 MFMAs, so the accumulator lands in the B-operand layout of O^T += V^T P^T: lane l
 //     holds query l%32. Key rows inside each 32-key block are loaded in a permuted order (bits 2
@@ -632,32 +634,34 @@ __device__ __forceinline__ float quantize_q_regs(const half8v (&q16f)[D / 16], i
 //   kF16s  rounds the online-softmax state (m, l and O) to binary16 after every 64-key tile.
 enum Variant : int { kProd = 0, kDump = 1, kKblk = 2, kSync = 3, kF16s = 4 };
 
+// One work item: the workgroup-sized piece (bx, by, bz) of the grid (query heads, query tiles in
+// reverse order, sequences) that a one-workgroup-per-item launch would give blockIdx.
 template <int D, bool KV8, int VAR, bool VN>
-__global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a) {
+__device__ __forceinline__ void prefill_item(const FwdArgs& a, char* smem, int bx, int by, int bz) {
   constexpr bool DUMP = VAR == kDump;
   constexpr bool KBLK = VAR == kKblk;
   constexpr bool SYNC = VAR == kSync;
   constexpr bool F16S = VAR == kF16s;
   using L = Smem<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
 
-  const int tid = threadIdx.x;
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));  // per item: nothing lane-dependent is kept live across items
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (scalar)
   const int hl = lane >> 5;   // half of the wave: selects 8 of the 16 keys of a k-step
   const int r32 = lane & 31;  // query row of this lane within the wave
 
   // XCD-friendly head order: consecutive workgroups cycle through the KV heads first
-  const int x = blockIdx.x;
+  const int x = bx;
   const int grp = a.hq / a.hkv;
-  const int b = blockIdx.z;
+  const int b = bz;
   const int n_ct = (a.max_seqlen_q + BM - 1) / BM;
   int h, c;
   if (a.hkv % 8 == 0 && n_ct >= 64) {
     // long sequences, KV heads a multiple of 8: workgroup lin of a sequence runs on XCD lin % 8,
     // which takes its KV heads j, j + 8, ... one at a time: the k-th workgroup it receives is
     // query tile c (heaviest first) of query head r % grp of its KV head k / (grp n_ct)
-    const int lin = x + a.hq * static_cast<int>(blockIdx.y);
+    const int lin = x + a.hq * by;
     const int j = lin & 7, k = lin >> 3;
     const int per_kv = grp * n_ct;
     const int r = k % per_kv;
@@ -665,7 +669,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
     h = (j + 8 * (k / per_kv)) * grp + r % grp;
   } else {
     h = grp * (x % a.hkv) + x / a.hkv;
-    c = n_ct - 1 - static_cast<int>(blockIdx.y);
+    c = n_ct - 1 - by;
   }
   const int q_begin = ld_uniform(a.cu_q, b);
   const int Lq = ld_uniform(a.cu_q, b + 1) - q_begin;
@@ -926,21 +930,86 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a
         l_row > 0.0f ? (wv.m_use + log2f(l_row)) * 0.69314718055994531f : -INFINITY;
 }
 
+
+// The fused kernel. PERS = false: one workgroup per work item (grid = items). PERS = true
+// (persistent, V^T path): as many workgroups as fit on the device at once, each taking items from
+// eight queues in the workspace, queue i holding the items g = i (mod 8) of the linear item order
+// g = x + hq (y + n_ct z) in increasing order -- the items the hardware would deal to XCD i. A
+// workgroup serves its own XCD's queue (the XCC id register) first and then the others, so an XCD
+// that runs faster than the rest takes over their last (lightest) items instead of idling: the
+// XCDs of one device do not run equally fast. Every workgroup leaves once all queues are empty.
+template <int D, bool KV8, int VAR, bool VN, bool PERS>
+__global__ __launch_bounds__(NW * 64, 1) void prefill_fwd_kernel(const FwdArgs a, int n_items) {
+  using L = Smem<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
+  if constexpr (!PERS) {
+    prefill_item<D, KV8, VAR, VN>(a, smem, blockIdx.x, blockIdx.y, blockIdx.z);
+  } else {
+    __shared__ int item_sh;
+    const int n_ct = (a.max_seqlen_q + BM - 1) / BM;
+    const int xq = static_cast<int>(__builtin_amdgcn_s_getreg(20 | (0 << 6) | (31 << 11)) & 7);  // XCC id
+    for (;;) {
+      if (threadIdx.x == 0) {
+        int g = -1;
+        for (int i = 0; i < 8 && g < 0; ++i) {
+          const int qi = (xq + i) & 7;
+          const int nq = qi < n_items ? (n_items - qi + 7) / 8 : 0;
+          if (nq == 0) continue;
+          const int k = atomicAdd(&a.sched[qi], 1);  // vector atomic; counters only grow
+          if (k < nq) g = qi + 8 * k;
+        }
+        item_sh = g;
+      }
+      __syncthreads();
+      const int g = item_sh;
+      __syncthreads();  // item_sh is rewritten only after every wave has read it
+      if (g < 0) break;
+      prefill_item<D, KV8, VAR, VN>(a, smem, g % a.hq, (g / a.hq) % n_ct, g / (a.hq * n_ct));
+    }
+  }
+}
+
+// Workgroups of one instance resident on the current device at once (cached per device).
+template <typename K>
+int resident_workgroups(K kern) {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int n_cu = 0, occ = 0;
+    if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(kern), NW * 64, 0) != hipSuccess)
+      return 0;
+    cache[dev] = n_cu * (occ > 0 ? occ : 1);
+  }
+  return cache[dev];
+}
+
+template <int D, bool KV8, int VAR, bool VN>
+hipError_t launch_i(const FwdArgs& a, dim3 grid, hipStream_t stream) {
+  const int n_items = static_cast<int>(grid.x * grid.y * grid.z);
+  if constexpr (!VN) {
+    if (a.sched != nullptr) {
+      const int n_res = resident_workgroups(prefill_fwd_kernel<D, KV8, VAR, VN, true>);
+      if (n_res > 0) {
+        prefill_fwd_kernel<D, KV8, VAR, VN, true><<<dim3(n_items < n_res ? n_items : n_res), dim3(NW * 64), 0, stream>>>(a, n_items);
+        return hipGetLastError();
+      }
+    }
+  }
+  prefill_fwd_kernel<D, KV8, VAR, VN, false><<<grid, dim3(NW * 64), 0, stream>>>(a, n_items);
+  return hipGetLastError();
+}
+
 template <int D, bool KV8, bool VN>
 hipError_t launch_v(const FwdArgs& a, dim3 grid, hipStream_t stream) {
   // the debug dump of the INT8 accumulators is compiled into a separate instance of the kernel
   // (with the dump the per-key instance runs: block-wise scales are per-key scales too)
-  if (a.dump != nullptr)
-    prefill_fwd_kernel<D, KV8, kDump, VN><<<grid, dim3(NW * 64), 0, stream>>>(a);
-  else if (a.sync_stages)
-    prefill_fwd_kernel<D, KV8, kSync, VN><<<grid, dim3(NW * 64), 0, stream>>>(a);
-  else if (a.state_fp16)
-    prefill_fwd_kernel<D, KV8, kF16s, VN><<<grid, dim3(NW * 64), 0, stream>>>(a);
-  else if (a.k_block > 0)
-    prefill_fwd_kernel<D, KV8, kKblk, VN><<<grid, dim3(NW * 64), 0, stream>>>(a);
-  else
-    prefill_fwd_kernel<D, KV8, kProd, VN><<<grid, dim3(NW * 64), 0, stream>>>(a);
-  return hipGetLastError();
+  if (a.dump != nullptr) return launch_i<D, KV8, kDump, VN>(a, grid, stream);
+  if (a.sync_stages) return launch_i<D, KV8, kSync, VN>(a, grid, stream);
+  if (a.state_fp16) return launch_i<D, KV8, kF16s, VN>(a, grid, stream);
+  if (a.k_block > 0) return launch_i<D, KV8, kKblk, VN>(a, grid, stream);
+  return launch_i<D, KV8, kProd, VN>(a, grid, stream);
 }
 
 template <int D, bool KV8>

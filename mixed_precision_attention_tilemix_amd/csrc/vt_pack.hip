@@ -16,6 +16,8 @@ __global__ __launch_bounds__(256) void vt_pack_kernel(const FwdArgs a) {
   constexpr int CPR = D / 8;  // 8-element chunks per key row
   __shared__ _Float16 tile[T][D + 8];
   const int n = blockIdx.x, b = blockIdx.y, hk = blockIdx.z;
+  // the fused kernel's work-queue counters start at zero (the fused kernel follows on the stream)
+  if (a.sched != nullptr && n == 0 && b == 0 && hk == 0 && threadIdx.x < 8) a.sched[threadIdx.x] = 0;
   const int k_begin = a.cu_k[b];
   const int Lk = a.cu_k[b + 1] - k_begin;
   const int j0 = n * T;

@@ -175,13 +175,14 @@ def test_workspace_size(lib):
     n = ctypes.c_int64(0)
     assert lib.tilemix_prefill_workspace_size(ctypes.byref(p), ctypes.byref(n)) == B.TILEMIX_OK
     # enough for either V path, i.e. the V^T path's: hkv * (ceil(total_k / 64) + batch) tiles of
-    # 64 x head_dim fp16 (the direct path needs none without an INT8 cache)
+    # 64 x head_dim fp16 and 256 bytes of work-queue counters (the direct path needs none without
+    # an INT8 cache)
     tiles = 2 * (256 // 64 + 1)
-    assert n.value == tiles * 64 * 128 * 2
+    assert n.value == tiles * 64 * 128 * 2 + 256
     p.kv_int8 = 1
     assert lib.tilemix_prefill_workspace_size(ctypes.byref(p), ctypes.byref(n)) == B.TILEMIX_OK
     # + the exact fp16 copy of K8 (total_k x hkv x head_dim); the direct path's K and V copies fit too
-    assert n.value == tiles * 64 * 128 * 2 + 256 * 2 * 128 * 2
+    assert n.value == tiles * 64 * 128 * 2 + 256 * 2 * 128 * 2 + 256
     assert n.value >= 2 * 256 * 2 * 128 * 2
     p.head_dim = 80
     assert lib.tilemix_prefill_workspace_size(ctypes.byref(p), ctypes.byref(n)) == B.TILEMIX_EUNSUPPORTED
