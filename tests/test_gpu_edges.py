@@ -27,7 +27,7 @@ def _cu(lens):
     return np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
 
 
-def run_case(lq, lk, hq, hk, d, bm, bn, g, causal, kv_int8, seed, v_path=0):
+def run_case(lq, lk, hq, hk, d, bm, bn, g, causal, kv_int8, seed, v_path=0, ws_fill=None):
     rng = np.random.default_rng(seed)
     Tq, Tk = sum(lq), sum(lk)
     q = rng.standard_normal((Tq, hq, d)).astype(np.float16)
@@ -61,6 +61,8 @@ def run_case(lq, lk, hq, hk, d, bm, bn, g, causal, kv_int8, seed, v_path=0):
     lse = torch.empty((hq, Tq), dtype=torch.float32, device="cuda")
     ws = torch.empty(max(256, B.tilemix_prefill_workspace_size(batch=len(lq), hkv=hk, head_dim=d, total_k=Tk,
                                                                kv_int8=kv_int8)), dtype=torch.uint8, device="cuda")
+    if ws_fill is not None:
+        ws.fill_(ws_fill)
     B.tilemix_prefill_fwd(q=t(q), q8=None, q_scale=None, k8=dk8, k_scale=dks, k=None if kv_int8 else t(k),
                           v=None if kv_int8 else t(v), v8=dv8, v_scale=dvs, route_words=words,
                           cu_seqlens_q=t(cu_q), cu_seqlens_k=t(cu_k), cu_mtiles=t(cu_m),
@@ -124,3 +126,13 @@ def test_random_unequal_lengths(seed):
     o2, l2, _, _ = run_case(**c, v_path=2)
     assert np.array_equal(o1.view(np.int32), o2.view(np.int32)), c
     assert np.array_equal(l1.view(np.int32), l2.view(np.int32)), c
+
+
+def test_vt_path_workspace_garbage():
+    # the V^T path keeps its work-queue counters in the workspace; whatever the workspace holds on
+    # entry, the pre-pass zeroes them, so a workspace filled with 0x7f bytes gives the same outputs
+    lq = lk = [900, 300]
+    first = run_case(lq, lk, 8, 2, 128, 128, 128, 1, True, False, seed=40, v_path=1)
+    again = run_case(lq, lk, 8, 2, 128, 128, 128, 1, True, False, seed=40, v_path=1, ws_fill=0x7F)
+    assert np.array_equal(first[0].view(np.int32), again[0].view(np.int32))
+    assert np.array_equal(first[1].view(np.int32), again[1].view(np.int32))
