@@ -117,7 +117,7 @@ def draw_unequal(seed):
                 causal=bool(rng.integers(0, 2)), kv_int8=bool(rng.integers(0, 2)), seed=6000 + seed)
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(40))
 def test_random_unequal_lengths(seed):
     # bottom-right causal alignment with L_q > L_k (rows without a legal key) and L_q < L_k, in
     # both V paths, which must agree bit for bit

@@ -47,7 +47,7 @@ def draw(seed):
                 seed=seed), bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
 
 
-CASES = [draw(s) for s in range(40)]
+CASES = [draw(s) for s in range(80)]
 
 
 def outputs(prob, v_path):
