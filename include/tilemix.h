@@ -184,7 +184,8 @@ typedef struct tilemix_fwd_params {
    * writes V transposed into the workspace, tile by tile; 2 = the kernel stages V rows as they
    * are and transposes them with its LDS reads (no pre-pass, no workspace without kv_int8);
    * 0 = the library chooses (2 when the V pre-pass would be a sizable share of the call: short
-   * sequences relative to the number of KV heads, 1 otherwise). Prefill only; decode ignores it. */
+   * sequences, at most 16k keys, relative to the number of KV heads; 1 otherwise). Prefill only;
+   * decode ignores it. */
   int32_t v_path;
 } tilemix_fwd_params;
 

@@ -85,14 +85,17 @@ WorkspaceLayout workspace_layout(const tilemix_fwd_params* p, bool v_direct) {
 }
 
 // Which V path a call takes. The V^T pre-pass reads and writes V once (about 4 bytes per key
-// row and channel); the direct path instead doubles the kernel's LDS reads of V, a cost that grows
-// with the work per key. The direct path wins while the work per key row (query-key pairs x query
-// heads / (keys x KV heads), estimated from the largest sequence) stays under 16384: measured,
-// 8k-token multi-head and GQA 4:1 sequences gain 1-5 %, 32k GQA 4:1 loses 1 %.
+// row and channel) and lets the fused kernel run persistent (its work queues are zeroed by the
+// pre-pass); the direct path instead doubles the kernel's LDS reads of V, a cost that grows with
+// the work per key. The direct path wins while the work per key row (query-key pairs x query
+// heads / (keys x KV heads), estimated from the largest sequence) stays at or under 16384 and the
+// sequences are at most 16k keys long. Measured (fused call, direct / V^T): four 4k multi-head
+// sequences 0.89, 8k multi-head 0.94, 8k GQA 4:1 0.98, 16k multi-head 1.00, 32k multi-head 1.01,
+// 16k GQA 4:1 1.01, 32k GQA 4:1 1.03, the 64k varlen batch 1.02.
 bool choose_v_direct(const tilemix_fwd_params* p) {
   if (p->v_path != 0) return p->v_path == 2;
   const double pairs = static_cast<double>(p->total_q) * p->max_seqlen_k * (p->causal ? 0.5 : 1.0);
-  return pairs * p->hq <= 16384.0 * static_cast<double>(p->total_k) * p->hkv;
+  return p->max_seqlen_k <= 16384 && pairs * p->hq <= 16384.0 * static_cast<double>(p->total_k) * p->hkv;
 }
 
 // Bytes of the decode workspace: per (sequence, KV head, key chunk, query row) the chunk's max,

@@ -202,6 +202,7 @@ def test_v_path_choice(lib):
     assert path(131072, 32, 8) == 1     # 128k
     assert path(16384, 28, 4, batch_total=65752) == 1  # the varlen batch
     assert path(8192, 32, 8) == 2 and path(8193, 32, 8) == 1  # the boundary: 16384 pairs per key row
+    assert path(16384, 32, 32) == 2 and path(32768, 32, 32) == 1  # and at most 16k keys
     assert path(8192, 32, 8, causal=False) == 1
     assert path(32768, 32, 8, v_path=2) == 2 and path(256, 2, 2, v_path=1) == 1
     assert path(256, 2, 2, v_path=3) == 0
